@@ -1,0 +1,108 @@
+"""fp64 CPU oracle for the GSPN 4-direction line scan -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may use
+this package.  The HIP library never imports, links or calls it.
+
+The arithmetic lives in ``gspn_oracle.c`` (plain C loops in fp64, OpenMP over
+(b, c) slices); this module compiles it with gcc and calls it through ctypes.
+Its header lists the passages of the pages it follows and the readings taken
+where they are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gspn_oracle.c")
+_LIB = os.path.join(_HERE, "libgspn_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle library in place (gcc, -O2, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def open_library(path: str):
+    """ctypes handle of an oracle library built from ``gspn_oracle.c``."""
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.gspn_oracle_fwd_f64.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
+    lib.gspn_oracle_fwd_f64.restype = ctypes.c_int
+    lib.gspn_oracle_slice_f64.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_uint32, ctypes.c_int32]
+    lib.gspn_oracle_slice_f64.restype = ctypes.c_int
+    lib.gspn_oracle_max_threads.argtypes = []
+    lib.gspn_oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            _lib = open_library(_LIB)
+    return _lib
+
+
+def _dptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _f64c(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def max_threads() -> int:
+    return _load().gspn_oracle_max_threads()
+
+
+def scan_fwd(x, w, lam, u, *, dirs: int = 15, groups: int = 1, cpw: int = 1,
+             nthreads: int = 0, lib=None) -> np.ndarray:
+    """y[B][C][H][W] in fp64.
+
+    x, lam, u: [B][C][H][W]; w: [popcount(dirs)][B][C/cpw][3][H][W].
+    """
+    x, w, lam, u = (_f64c(a) for a in (x, w, lam, u))
+    B, C, H, W = x.shape
+    nd = bin(dirs & 15).count("1")
+    if lam.shape != x.shape or u.shape != x.shape:
+        raise ValueError("x, lam, u must share one shape")
+    if cpw < 1 or C % cpw or w.shape != (nd, B, C // cpw, 3, H, W):
+        raise ValueError(f"w has shape {w.shape}, expected {(nd, B, C // max(cpw, 1), 3, H, W)}")
+    y = np.empty_like(x)
+    rc = (lib or _load()).gspn_oracle_fwd_f64(_dptr(x), _dptr(w), _dptr(lam), _dptr(u), _dptr(y),
+                                     B, C, H, W, dirs, groups, cpw, nthreads)
+    if rc:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return y
+
+
+def slice_fwd(x, w, lam, u, *, dirs: int = 15, groups: int = 1) -> np.ndarray:
+    """One slice: x, lam, u [H][W]; w [popcount(dirs)][3][H][W] -> y [H][W]."""
+    x, w, lam, u = (_f64c(a) for a in (x, w, lam, u))
+    H, W = x.shape
+    nd = bin(dirs & 15).count("1")
+    if w.shape != (nd, 3, H, W):
+        raise ValueError(f"w has shape {w.shape}, expected {(nd, 3, H, W)}")
+    y = np.empty_like(x)
+    rc = _load().gspn_oracle_slice_f64(_dptr(x), _dptr(w), _dptr(lam), _dptr(u), _dptr(y),
+                                       H, W, dirs, groups)
+    if rc:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return y

@@ -1,0 +1,242 @@
+/*
+ * gspn_oracle.c -- plain fp64 CPU oracle for the GSPN 4-direction line scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library.  It shares no
+ * code, header or constant with the HIP library; the product path never
+ * calls it.
+ *
+ * What it computes (written from the method's definition, not from any
+ * listing):
+ *
+ *  - "Parallel Sequence Modeling via Generalized Spatial Propagation
+ *    Network" (CVPR 2025 paper notes), section "Key design 1: stability-
+ *    context condition": the 2D linear propagation h_i = w_i h_{i-1} +
+ *    lambda_i (.) x_i over the lines of the grid; each w_i is made
+ *    row-stochastic by applying a sigmoid to the non-zero entries of each of
+ *    its rows and dividing by the row sum.
+ *  - same notes, section "Key design 2: tridiagonal matrix + 4-direction line
+ *    scan": each pixel connects to the 3 adjacent pixels of the previous line
+ *    (for the top-to-bottom scan: top-left, top, top-right), so w_i is
+ *    tridiagonal; the scan runs in 4 directions and the results are merged.
+ *  - same notes, section "Key design 3: global/local variants": the local
+ *    variant splits one spatial dimension into g non-overlapping groups that
+ *    propagate independently.
+ *
+ * Readings taken where the pages are silent (each one is a convention the
+ * HIP library documents identically):
+ *  - the previous state before the first line of a group is zero, so the
+ *    first line of every group is h = lambda * x (its raw taps are unused);
+ *  - the weights of line i are stored at the destination pixel of line i;
+ *  - tap t = 0, 1, 2 couples position p to position p-1, p, p+1 of the
+ *    previous line, in absolute grid coordinates for all four directions;
+ *  - at a line border the missing tap is dropped and the remaining sigmoids
+ *    are renormalised (a line of length 1 has the single weight 1);
+ *  - the local groups split each direction's scan axis into g equal
+ *    segments; the state restarts at each segment's first line;
+ *  - the merge is y = u * sum over the enabled directions of h_dir, with
+ *    lambda and u shared by all directions and the raw taps per direction;
+ *  - channel c uses weight set c / cpw (compact multi-channel mode).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { DIR_TB = 0, DIR_BT = 1, DIR_LR = 2, DIR_RL = 3 };
+
+/* Grid coordinates (r, q) of position p on line i of direction d. */
+static void pixel_of(int d, int64_t H, int64_t W, int64_t i, int64_t p, int64_t *r, int64_t *q)
+{
+    switch (d) {
+    case DIR_TB: *r = i;         *q = p;         break;
+    case DIR_BT: *r = H - 1 - i; *q = p;         break;
+    case DIR_LR: *r = p;         *q = i;         break;
+    default:     *r = p;         *q = W - 1 - i; break;
+    }
+}
+
+static double sigmoid(double a) { return 1.0 / (1.0 + exp(-a)); }
+
+/*
+ * One (b, c) slice.
+ *   x, lam, u : [H][W]
+ *   w         : [popcount(dirs)][3][H][W], raw taps of this slice's weight
+ *               set, one slab per enabled direction in ascending bit order
+ *   y         : [H][W] output
+ *   work      : 3 * max(H, W) + H * W doubles of scratch
+ * Returns 0, or -1 on a bad argument.
+ */
+static int slice_fwd(const double *x, const double *w, const double *lam, const double *u,
+                     double *y, int64_t H, int64_t W, uint32_t dirs, int32_t groups, double *work)
+{
+    const int64_t HW = H * W;
+    const int64_t mmax = H > W ? H : W;
+    double *h = work;
+    double *hn = work + mmax;
+    double *acc = work + 2 * mmax;
+    memset(acc, 0, sizeof(double) * (size_t)HW);
+
+    int slab = 0;
+    for (int d = 0; d < 4; ++d) {
+        if (!((dirs >> d) & 1u))
+            continue;
+        const double *wd = w + (int64_t)slab * 3 * HW;
+        ++slab;
+        const int64_t n = (d == DIR_TB || d == DIR_BT) ? H : W; /* lines */
+        const int64_t m = (d == DIR_TB || d == DIR_BT) ? W : H; /* positions per line */
+        if (n % groups)
+            return -1;
+        const int64_t L = n / groups; /* lines per group */
+
+        for (int64_t i = 0; i < n; ++i) {
+            for (int64_t p = 0; p < m; ++p) {
+                int64_t r, q;
+                pixel_of(d, H, W, i, p, &r, &q);
+                const double xl = lam[r * W + q] * x[r * W + q];
+                if (i % L == 0) {
+                    hn[p] = xl; /* zero state before a group's first line */
+                    continue;
+                }
+                /* sigmoid of the taps that exist, then divide by their sum */
+                double s[3] = {0.0, 0.0, 0.0};
+                double ssum = 0.0;
+                for (int t = 0; t < 3; ++t) {
+                    const int64_t pp = p + t - 1;
+                    if (pp < 0 || pp >= m)
+                        continue;
+                    s[t] = sigmoid(wd[(int64_t)t * HW + r * W + q]);
+                    ssum += s[t];
+                }
+                double v = xl;
+                for (int t = 0; t < 3; ++t) {
+                    const int64_t pp = p + t - 1;
+                    if (pp < 0 || pp >= m)
+                        continue;
+                    v += (s[t] / ssum) * h[pp];
+                }
+                hn[p] = v;
+            }
+            for (int64_t p = 0; p < m; ++p) {
+                int64_t r, q;
+                pixel_of(d, H, W, i, p, &r, &q);
+                acc[r * W + q] += hn[p];
+                h[p] = hn[p];
+            }
+        }
+    }
+    for (int64_t j = 0; j < HW; ++j)
+        y[j] = u[j] * acc[j];
+    return 0;
+}
+
+static int ndirs_of(uint32_t dirs)
+{
+    int k = 0;
+    for (int d = 0; d < 4; ++d)
+        k += (int)((dirs >> d) & 1u);
+    return k;
+}
+
+static int check_args(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs,
+                      int32_t groups, int32_t cpw)
+{
+    if (B <= 0 || C <= 0 || H <= 0 || W <= 0)
+        return -2;
+    if (dirs == 0 || (dirs & ~15u))
+        return -3;
+    if (groups < 1)
+        return -4;
+    if (((dirs & 3u) && H % groups) || ((dirs & 12u) && W % groups))
+        return -4;
+    if (cpw < 1 || C % cpw)
+        return -5;
+    return 0;
+}
+
+/*
+ * Whole tensors.
+ *   x, lam, u, y : [B][C][H][W]
+ *   w            : [popcount(dirs)][B][C/cpw][3][H][W]
+ * nthreads <= 0 uses the OpenMP default.  Returns 0 or a negative code.
+ */
+int gspn_oracle_fwd_f64(const double *x, const double *w, const double *lam, const double *u,
+                        double *y, int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs,
+                        int32_t groups, int32_t cpw, int nthreads)
+{
+    int rc = check_args(B, C, H, W, dirs, groups, cpw);
+    if (rc)
+        return rc;
+    if (!x || !w || !lam || !u || !y)
+        return -1;
+    const int64_t HW = H * W;
+    const int64_t Cw = C / cpw;
+    const int nd = ndirs_of(dirs);
+    const int64_t mmax = H > W ? H : W;
+    const int64_t nslices = B * C;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel reduction(| : bad)
+    {
+        double *work = (double *)malloc(sizeof(double) * (size_t)(2 * mmax + HW));
+        /* per-slice gather of this slice's weight slabs */
+        double *wsl = (double *)malloc(sizeof(double) * (size_t)(nd * 3 * HW));
+        if (!work || !wsl) {
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t s = 0; s < nslices; ++s) {
+                const int64_t b = s / C, c = s % C, k = c / cpw;
+                for (int j = 0; j < nd; ++j)
+                    memcpy(wsl + (int64_t)j * 3 * HW,
+                           w + (((int64_t)j * B + b) * Cw + k) * 3 * HW,
+                           sizeof(double) * (size_t)(3 * HW));
+                const int64_t off = s * HW;
+                if (slice_fwd(x + off, wsl, lam + off, u + off, y + off, H, W, dirs, groups, work))
+                    bad = 1;
+            }
+        }
+        free(work);
+        free(wsl);
+    }
+    return bad ? -2 : 0;
+}
+
+/*
+ * One slice from its own inputs (for sampled checks on large tensors).
+ *   x, lam, u, y : [H][W];  w : [popcount(dirs)][3][H][W]
+ */
+int gspn_oracle_slice_f64(const double *x, const double *w, const double *lam, const double *u,
+                          double *y, int64_t H, int64_t W, uint32_t dirs, int32_t groups)
+{
+    int rc = check_args(1, 1, H, W, dirs, groups, 1);
+    if (rc)
+        return rc;
+    if (!x || !w || !lam || !u || !y)
+        return -1;
+    const int64_t mmax = H > W ? H : W;
+    double *work = (double *)malloc(sizeof(double) * (size_t)(2 * mmax + H * W));
+    if (!work)
+        return -2;
+    rc = slice_fwd(x, w, lam, u, y, H, W, dirs, groups, work);
+    free(work);
+    return rc;
+}
+
+int gspn_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
