@@ -1,0 +1,161 @@
+/*
+ * gspn.h -- C ABI of the MI355X (gfx950) GSPN line-scan library, libgspn.so.
+ *
+ * The operator is the 2D linear propagation of the Generalized Spatial
+ * Propagation Network:
+ *
+ *   "Parallel Sequence Modeling via Generalized Spatial Propagation Network"
+ *   (CVPR 2025 paper notes):
+ *     - "Key design 1: stability-context condition": h_i = w_i h_{i-1} +
+ *       lambda_i (.) x_i along the lines of the grid, with each w_i made
+ *       row-stochastic by a sigmoid on the non-zero entries of each row
+ *       followed by division by the row sum;
+ *     - "Key design 2: tridiagonal matrix + 4-direction line scan": each pixel
+ *       connects to the 3 adjacent pixels of the previous line (top-left,
+ *       top, top-right for the top-to-bottom scan); the scan runs in four
+ *       directions and the directions are merged;
+ *     - "Key design 3: global/local variants": the local variant splits one
+ *       spatial dimension into g groups that propagate independently.
+ *   "GSPN-2: Efficient Parallel Sequence Modeling" (author response,
+ *   paragraphs "How Channel-shared Weight Mitigates the Concurrency
+ *   Bottleneck?" and "Justification for Channel-Agnostic Propagation"): one
+ *   propagation weight map shared by several channels, channel diversity kept
+ *   by the per-channel gains lambda (the compact multi-channel mode).
+ *
+ * Exact definition computed by gspn_scan_fwd (readings fixed by this ABI where
+ * the pages are silent):
+ *
+ *   For each enabled direction d, batch b, channel c (weight set k = c / cpw):
+ *     TB: line i = row i,      position p = column;   n = H lines of m = W
+ *     BT: line i = row H-1-i,  position p = column;   n = H, m = W
+ *     LR: line i = column i,   position p = row;      n = W, m = H
+ *     RL: line i = column W-1-i, position p = row;    n = W, m = H
+ *     L = n / groups lines per group.
+ *     If i mod L == 0:  h_i[p] = lam[p] * x[p]            (state restarts)
+ *     else:             h_i[p] = sum_t w_t * h_{i-1}[p+t-1] + lam[p] * x[p]
+ *       over the taps t in {0,1,2} with 0 <= p+t-1 < m, where
+ *       w_t = sigmoid(a_t) / (sum of sigmoid(a_s) over the existing taps s)
+ *       and a_t = w_raw[slab(d)][b][k][t][pixel of (i, p)].
+ *   y[b][c][r][q] = u[b][c][r][q] * sum over enabled d of h_d at pixel (r, q).
+ *
+ *   Tap t = 0, 1, 2 couples position p to positions p-1, p, p+1 of the
+ *   previous line in absolute grid coordinates, for all four directions.
+ *   The raw taps of a group's first line and of taps that fall outside the
+ *   line are never used and may hold any value (NaN and Inf included).
+ *   lam and u are shared by all directions; w_raw has one slab per enabled
+ *   direction.
+ *
+ * Tensor layouts (all C-contiguous, all in the same dtype):
+ *   x, lam, u, y : [B][C][H][W]
+ *   w_raw        : [popcount(dirs)][B][C / ch_per_weight][3][H][W], one slab
+ *                  per enabled direction, in ascending bit order.
+ *
+ * Arithmetic: inputs are widened to fp32, every product and sum is formed in
+ * fp32, and y is rounded to the I/O dtype with round-to-nearest-even.
+ * Results match the exact definition to fp32 rounding for raw taps >= -40;
+ * rows whose taps are more negative take a slower exact-form branch.
+ *
+ * Memory and streams: every pointer is a device pointer owned by the caller;
+ * base pointers must be 16-byte aligned; y must not overlap any input.  Calls
+ * only enqueue work on `stream` and never synchronise; a kernel fault shows
+ * at the caller's next synchronisation.  Shapes with H <= 64 and W <= 64 run
+ * one fused kernel and allocate nothing.  Larger shapes run the general path,
+ * which takes an fp32 workspace of popcount(dirs) * B*C*H*W * 4 bytes
+ * stream-ordered (hipMallocAsync / hipFreeAsync on `stream`).
+ * The library keeps no other state: calls on different streams may run
+ * concurrently.  Results are deterministic (fixed summation order, no atomics).
+ *
+ * Errors: every argument is checked on the host before anything is enqueued;
+ * on an error nothing is launched and y is untouched.  A failed HIP call
+ * returns GSPN_ERR_HIP and leaves its text in gspn_last_error() (per thread).
+ */
+#ifndef GSPN_H
+#define GSPN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+#define GSPN_VERSION 1
+
+typedef enum { GSPN_F32 = 0, GSPN_BF16 = 1 } gspn_dtype;
+
+enum {
+    GSPN_DIR_TB = 1, /* top to bottom */
+    GSPN_DIR_BT = 2, /* bottom to top */
+    GSPN_DIR_LR = 4, /* left to right */
+    GSPN_DIR_RL = 8, /* right to left */
+    GSPN_DIR_ALL = 15
+};
+
+enum {
+    GSPN_OK = 0,
+    GSPN_ERR_NULL = -1,   /* a pointer is null */
+    GSPN_ERR_SHAPE = -2,  /* B, C, H or W <= 0, H or W > GSPN_MAX_SIDE, B*C > 2^22 */
+    GSPN_ERR_DIRS = -3,   /* dirs is 0 or has a bit above 0xF */
+    GSPN_ERR_GROUPS = -4, /* groups < 1, or it does not divide a scanned side */
+    GSPN_ERR_CPW = -5,    /* ch_per_weight < 1 or it does not divide C */
+    GSPN_ERR_DTYPE = -6,  /* unknown dtype */
+    GSPN_ERR_ALIGN = -7,  /* a base pointer is not 16-byte aligned */
+    GSPN_ERR_ALIAS = -8,  /* y overlaps an input */
+    GSPN_ERR_HIP = -9,    /* a HIP call failed; see gspn_last_error() */
+    GSPN_ERR_PATH = -10   /* unknown path, or the forced path cannot take this shape */
+};
+
+/* Largest H and W accepted. */
+#define GSPN_MAX_SIDE 4096
+
+/* Kernel paths for gspn_scan_fwd_path. */
+enum {
+    GSPN_PATH_AUTO = 0,    /* what gspn_scan_fwd uses */
+    GSPN_PATH_FUSED = 1,   /* one fused 4-direction kernel; needs H <= 64 and W <= 64 */
+    GSPN_PATH_GENERAL = 2  /* per-direction kernels + merge; any shape; uses a workspace */
+};
+
+/*
+ * Forward 4-direction scan (definition above).
+ *   x, lam, u : [B][C][H][W] inputs;  w_raw : raw taps (layout above)
+ *   y         : [B][C][H][W] output, fully overwritten
+ *   dirs      : bitmask of GSPN_DIR_*, 1..15
+ *   groups    : g >= 1; must divide H if TB or BT is enabled, and W if LR or
+ *               RL is enabled (g = 1 is the global scan)
+ *   ch_per_weight : channels per weight set, divides C (1 = per-channel
+ *               weights, C = one map shared by every channel)
+ *   dtype     : gspn_dtype of all five tensors
+ *   stream    : HIP stream the work is enqueued on (0 = null stream)
+ * Returns GSPN_OK or a negative GSPN_ERR_* code.
+ */
+int gspn_scan_fwd(const void *x, const void *w_raw, const void *lam, const void *u, void *y,
+                  int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
+                  int32_t ch_per_weight, int32_t dtype, hipStream_t stream);
+
+/* Same operation on a chosen kernel path (GSPN_PATH_*); used to cross-check
+ * the paths against each other.  GSPN_ERR_PATH if the path cannot run the
+ * shape. */
+int gspn_scan_fwd_path(const void *x, const void *w_raw, const void *lam, const void *u, void *y,
+                       int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
+                       int32_t ch_per_weight, int32_t dtype, int32_t path, hipStream_t stream);
+
+/* The path gspn_scan_fwd would take for these sizes (GSPN_PATH_FUSED or
+ * GSPN_PATH_GENERAL), or a negative error code for invalid sizes. */
+int gspn_select_path(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
+                     int32_t ch_per_weight, int32_t dtype);
+
+/* Static text for a status code. */
+const char *gspn_status_string(int status);
+
+/* Detail of the calling thread's last failure ("" if none). */
+const char *gspn_last_error(void);
+
+/* GSPN_VERSION of the built library. */
+int gspn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSPN_H */

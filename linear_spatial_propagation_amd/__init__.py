@@ -1,0 +1,70 @@
+"""GSPN 2D line-scan propagation on MI355X (gfx950).
+
+    y = scan_fwd(x, w_raw, lam, u, dirs=15, groups=1, ch_per_weight=1)
+
+computes the 4-direction line recurrence of the Generalized Spatial
+Propagation Network with hand-written HIP kernels (libgspn.so, C ABI in
+include/gspn.h).  PyTorch supplies device memory and the current stream;
+this wrapper only checks tensors and passes pointers.
+
+Tensors (same dtype, float32 or bfloat16, contiguous, on one GPU):
+  x, lam, u : [B, C, H, W]
+  w_raw     : [popcount(dirs), B, C // ch_per_weight, 3, H, W]
+"""
+from __future__ import annotations
+
+from . import _lib
+from ._lib import (DIR_ALL, DIR_BT, DIR_LR, DIR_RL, DIR_TB, PATH_AUTO, PATH_FUSED, PATH_GENERAL,
+                   GspnError, load, select_path)
+
+__all__ = ["scan_fwd", "select_path", "load", "GspnError", "DIR_TB", "DIR_BT", "DIR_LR", "DIR_RL",
+           "DIR_ALL", "PATH_AUTO", "PATH_FUSED", "PATH_GENERAL"]
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return _lib.GSPN_BF16
+    if t.dtype == torch.float32:
+        return _lib.GSPN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def scan_fwd(x, w_raw, lam, u, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1,
+             out=None, path: int = PATH_AUTO):
+    """Forward GSPN scan on the current HIP stream; returns y [B, C, H, W]."""
+    import torch
+    tensors = {"x": x, "w_raw": w_raw, "lam": lam, "u": u}
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU (HIP) device")
+    for name, t in tensors.items():
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, x is on {dev}")
+        if t.dtype != x.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, x has {x.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if x.dim() != 4:
+        raise ValueError("x must be [B, C, H, W]")
+    B, C, H, W = x.shape
+    nd = bin(dirs & 15).count("1")
+    if lam.shape != x.shape or u.shape != x.shape:
+        raise ValueError("lam and u must have x's shape")
+    if ch_per_weight < 1 or C % ch_per_weight:
+        raise ValueError("ch_per_weight must divide C")
+    if tuple(w_raw.shape) != (nd, B, C // ch_per_weight, 3, H, W):
+        raise ValueError(f"w_raw has shape {tuple(w_raw.shape)}, expected "
+                         f"{(nd, B, C // ch_per_weight, 3, H, W)}")
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or out.device != dev or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = _lib.scan_fwd_ptr(x.data_ptr(), w_raw.data_ptr(), lam.data_ptr(), u.data_ptr(),
+                               out.data_ptr(), B, C, H, W, dirs=dirs, groups=groups,
+                               ch_per_weight=ch_per_weight, dtype=_dtype_code(x), path=path,
+                               stream=stream)
+    _lib.check(rc)
+    return out

@@ -1,0 +1,85 @@
+"""ctypes binding of libgspn.so (the C ABI declared in include/gspn.h).
+
+Argument marshalling only: every step of the operator runs in the HIP
+kernels of the shared library.  If the library is missing this module raises;
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgspn.so")
+
+GSPN_F32 = 0
+GSPN_BF16 = 1
+PATH_AUTO = 0
+PATH_FUSED = 1
+PATH_GENERAL = 2
+DIR_TB, DIR_BT, DIR_LR, DIR_RL, DIR_ALL = 1, 2, 4, 8, 15
+
+EXPORTED = ("gspn_scan_fwd", "gspn_scan_fwd_path", "gspn_select_path", "gspn_status_string",
+            "gspn_last_error", "gspn_version")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class GspnError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(text)
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgspn.so once; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m linear_spatial_propagation_amd.build`")
+        lib = ctypes.CDLL(path)
+        vp, i64, u32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int32
+        lib.gspn_scan_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, u32, i32, i32, i32, vp]
+        lib.gspn_scan_fwd.restype = ctypes.c_int
+        lib.gspn_scan_fwd_path.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, u32, i32, i32, i32,
+                                           i32, vp]
+        lib.gspn_scan_fwd_path.restype = ctypes.c_int
+        lib.gspn_select_path.argtypes = [i64, i64, i64, i64, u32, i32, i32, i32]
+        lib.gspn_select_path.restype = ctypes.c_int
+        lib.gspn_status_string.argtypes = [ctypes.c_int]
+        lib.gspn_status_string.restype = ctypes.c_char_p
+        lib.gspn_last_error.argtypes = []
+        lib.gspn_last_error.restype = ctypes.c_char_p
+        lib.gspn_version.argtypes = []
+        lib.gspn_version.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load().gspn_status_string(status).decode()
+
+
+def check(status: int) -> None:
+    if status != 0:
+        lib = load()
+        detail = lib.gspn_last_error().decode()
+        msg = lib.gspn_status_string(status).decode()
+        raise GspnError(status, msg + (f" [{detail}]" if detail else ""))
+
+
+def scan_fwd_ptr(x: int, w: int, lam: int, u: int, y: int, B: int, C: int, H: int, W: int, *,
+                 dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1, dtype: int = GSPN_BF16,
+                 path: int = PATH_AUTO, stream: int = 0) -> int:
+    """Raw call on device pointers; returns the status code."""
+    return load().gspn_scan_fwd_path(x, w, lam, u, y, B, C, H, W, dirs, groups, ch_per_weight,
+                                     dtype, path, stream)
+
+
+def select_path(B, C, H, W, *, dirs=DIR_ALL, groups=1, ch_per_weight=1, dtype=GSPN_BF16) -> int:
+    return load().gspn_select_path(B, C, H, W, dirs, groups, ch_per_weight, dtype)

@@ -1,0 +1,132 @@
+// gspn_api.hip -- C ABI of libgspn: argument validation and kernel dispatch.
+//
+// The operator and every convention are specified in include/gspn.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gspn_kernels.h"
+#include "../../include/gspn.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+void set_error(const char* what, hipError_t e) {
+    snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+void set_error_text(const char* text) { snprintf(g_last_error, sizeof(g_last_error), "%s", text); }
+
+int popcount4(uint32_t d) { return (int)((d & 1u) + ((d >> 1) & 1u) + ((d >> 2) & 1u) + ((d >> 3) & 1u)); }
+
+// Host-side checks of sizes and options (no pointers).
+int check_sizes(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
+                int32_t cpw, int32_t dtype) {
+    if (B <= 0 || C <= 0 || H <= 0 || W <= 0) return GSPN_ERR_SHAPE;
+    if (H > GSPN_MAX_SIDE || W > GSPN_MAX_SIDE) return GSPN_ERR_SHAPE;
+    // one workgroup per slice (or per slice and direction) of 256 threads:
+    // the launch must stay below 2^32 work-items
+    if (B > (1LL << 22) / C) return GSPN_ERR_SHAPE;                     // B*C <= 2^22
+    if (B * C > (int64_t)(1LL << 62) / (H * W * 4 * 4)) return GSPN_ERR_SHAPE;
+    if (dirs == 0 || (dirs & ~15u)) return GSPN_ERR_DIRS;
+    if (groups < 1) return GSPN_ERR_GROUPS;
+    if ((dirs & 3u) && H % groups) return GSPN_ERR_GROUPS;
+    if ((dirs & 12u) && W % groups) return GSPN_ERR_GROUPS;
+    if (cpw < 1 || C % cpw) return GSPN_ERR_CPW;
+    if (dtype != GSPN_F32 && dtype != GSPN_BF16) return GSPN_ERR_DTYPE;
+    return GSPN_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+int auto_path(int64_t H, int64_t W) {
+    return (H <= gspn::kFusedMaxSide && W <= gspn::kFusedMaxSide) ? GSPN_PATH_FUSED : GSPN_PATH_GENERAL;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gspn_version(void) { return GSPN_VERSION; }
+
+const char* gspn_last_error(void) { return g_last_error; }
+
+const char* gspn_status_string(int status) {
+    switch (status) {
+        case GSPN_OK: return "GSPN_OK";
+        case GSPN_ERR_NULL: return "GSPN_ERR_NULL: a pointer is null";
+        case GSPN_ERR_SHAPE: return "GSPN_ERR_SHAPE: a size is <= 0, above GSPN_MAX_SIDE, or overflows";
+        case GSPN_ERR_DIRS: return "GSPN_ERR_DIRS: dirs must be a non-zero mask of bits 0..3";
+        case GSPN_ERR_GROUPS: return "GSPN_ERR_GROUPS: groups must be >= 1 and divide each scanned side";
+        case GSPN_ERR_CPW: return "GSPN_ERR_CPW: ch_per_weight must be >= 1 and divide C";
+        case GSPN_ERR_DTYPE: return "GSPN_ERR_DTYPE: unknown dtype";
+        case GSPN_ERR_ALIGN: return "GSPN_ERR_ALIGN: a base pointer is not 16-byte aligned";
+        case GSPN_ERR_ALIAS: return "GSPN_ERR_ALIAS: y overlaps an input";
+        case GSPN_ERR_HIP: return "GSPN_ERR_HIP: a HIP call failed (see gspn_last_error)";
+        case GSPN_ERR_PATH: return "GSPN_ERR_PATH: unknown path, or the path cannot run this shape";
+        default: return "unknown GSPN status";
+    }
+}
+
+int gspn_select_path(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
+                     int32_t ch_per_weight, int32_t dtype) {
+    const int rc = check_sizes(B, C, H, W, dirs, groups, ch_per_weight, dtype);
+    return rc ? rc : auto_path(H, W);
+}
+
+int gspn_scan_fwd_path(const void* x, const void* w_raw, const void* lam, const void* u, void* y,
+                       int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
+                       int32_t ch_per_weight, int32_t dtype, int32_t path, hipStream_t stream) {
+    g_last_error[0] = '\0';
+    int rc = check_sizes(B, C, H, W, dirs, groups, ch_per_weight, dtype);
+    if (rc) return rc;
+    if (!x || !w_raw || !lam || !u || !y) return GSPN_ERR_NULL;
+    const void* ptrs[5] = {x, w_raw, lam, u, y};
+    for (const void* q : ptrs)
+        if ((uintptr_t)q & 15u) return GSPN_ERR_ALIGN;
+    const size_t es = dtype == GSPN_BF16 ? 2 : 4;
+    const size_t E = (size_t)B * C * H * W;
+    const size_t nbytes = E * es;
+    const size_t wbytes = (size_t)popcount4(dirs) * B * (C / ch_per_weight) * 3 * H * W * es;
+    if (overlaps(y, nbytes, x, nbytes) || overlaps(y, nbytes, lam, nbytes) ||
+        overlaps(y, nbytes, u, nbytes) || overlaps(y, nbytes, w_raw, wbytes))
+        return GSPN_ERR_ALIAS;
+    if (path == GSPN_PATH_AUTO) path = auto_path(H, W);
+    if (path != GSPN_PATH_FUSED && path != GSPN_PATH_GENERAL) return GSPN_ERR_PATH;
+    if (path == GSPN_PATH_FUSED && auto_path(H, W) != GSPN_PATH_FUSED) return GSPN_ERR_PATH;
+
+    gspn::ScanArgs a;
+    a.x = x; a.w = w_raw; a.lam = lam; a.u = u; a.y = y;
+    a.B = (int)B; a.C = (int)C; a.H = (int)H; a.W = (int)W;
+    a.dirs = dirs; a.groups = groups; a.cpw = ch_per_weight; a.bf16 = dtype == GSPN_BF16;
+
+    if (path == GSPN_PATH_FUSED) {
+        const hipError_t e = gspn::launch_fused(a, stream);
+        if (e != hipSuccess) { set_error("fused kernel launch", e); return GSPN_ERR_HIP; }
+        return GSPN_OK;
+    }
+    // general path: stream-ordered fp32 workspace, one plane per direction
+    float* planes = nullptr;
+    const size_t pbytes = (size_t)popcount4(dirs) * E * sizeof(float);
+    hipError_t e = hipMallocAsync((void**)&planes, pbytes, stream);
+    if (e != hipSuccess) { set_error("hipMallocAsync(workspace)", e); return GSPN_ERR_HIP; }
+    e = gspn::launch_general(a, planes, stream);
+    const hipError_t ef = hipFreeAsync(planes, stream);
+    if (e != hipSuccess) { set_error("general kernel launch", e); return GSPN_ERR_HIP; }
+    if (ef != hipSuccess) { set_error("hipFreeAsync(workspace)", ef); return GSPN_ERR_HIP; }
+    return GSPN_OK;
+}
+
+int gspn_scan_fwd(const void* x, const void* w_raw, const void* lam, const void* u, void* y,
+                  int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
+                  int32_t ch_per_weight, int32_t dtype, hipStream_t stream) {
+    return gspn_scan_fwd_path(x, w_raw, lam, u, y, B, C, H, W, dirs, groups, ch_per_weight, dtype,
+                              GSPN_PATH_AUTO, stream);
+}
+
+}  // extern "C"

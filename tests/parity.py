@@ -1,0 +1,78 @@
+"""Shared helpers of the GPU parity tests: upload, run, compare.
+
+The comparison metric.  For every output element i, with the oracle value
+yhat_i (fp64) and the device value y_i widened to fp64:
+
+    r_i   = |y_i - yhat_i|                                   (fp32 I/O)
+    r_i   = max(0, |y_i - yhat_i| - ulp_bf16(y_i) / 2)       (bf16 I/O)
+    err   = max_i  r_i / max(|yhat_i|, 0.1 * rms(yhat))
+
+For bf16 I/O the final rounding of y to bf16 is exact-by-definition (the
+half-ulp is subtracted), so err measures the fp32 accumulation error of the
+path; the floor 0.1 * rms keeps outputs that cancel to ~0 from dividing by
+~0.  Tolerances: err <= 1e-4 for fp32 I/O, err <= 2e-3 for bf16 I/O, and no
+NaN or Inf anywhere.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from linear_spatial_propagation_amd.inputs import bf16_bits_to_f32
+
+TOL = {"f32": 1e-4, "bf16": 2e-3}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def ulp_bf16(y: np.ndarray) -> np.ndarray:
+    m, e = np.frexp(np.abs(y))            # |y| = m * 2^e, m in [0.5, 1)
+    return np.where(y == 0, 0.0, np.ldexp(1.0, e - 8))
+
+
+def parity_error(y: np.ndarray, yhat: np.ndarray, dtype: str) -> float:
+    y = np.asarray(y, dtype=np.float64)
+    yhat = np.asarray(yhat, dtype=np.float64)
+    if y.shape != yhat.shape:
+        raise AssertionError(f"shape {y.shape} != {yhat.shape}")
+    if not np.all(np.isfinite(y)):
+        return float("inf")
+    diff = np.abs(y - yhat)
+    if dtype == "bf16":
+        diff = np.maximum(0.0, diff - 0.5 * ulp_bf16(y))
+    rms = float(np.sqrt(np.mean(yhat * yhat))) if yhat.size else 0.0
+    scale = np.maximum(np.abs(yhat), 0.1 * rms)
+    scale = np.where(scale == 0, 1.0, scale)
+    return float((diff / scale).max()) if y.size else 0.0
+
+
+def to_device(a: np.ndarray, dtype: str):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype == "bf16":
+        t = t.view(torch.bfloat16)
+    return t.cuda()
+
+
+def from_device(t, dtype: str) -> np.ndarray:
+    import torch
+    if dtype == "bf16":
+        return bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def run_workload(wl, path: int = 0):
+    """Upload a Workload, run the HIP scan, return y as fp64 numpy."""
+    import torch
+    import linear_spatial_propagation_amd as gspn
+    x = to_device(wl.x_store, wl.dtype)
+    w = to_device(wl.w_store, wl.dtype)
+    lam = to_device(wl.lam_store, wl.dtype)
+    u = to_device(wl.u_store, wl.dtype)
+    y = gspn.scan_fwd(x, w, lam, u, dirs=wl.dirs, groups=wl.groups, ch_per_weight=wl.cpw, path=path)
+    torch.cuda.synchronize()
+    return from_device(y, wl.dtype)

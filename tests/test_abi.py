@@ -1,0 +1,104 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects every invalid argument on the host before any launch.
+
+Calls here only pass invalid arguments (or fake pointers with invalid
+arguments), which the library rejects before touching the HIP runtime.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_spatial_propagation_amd as gspn
+from linear_spatial_propagation_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gspn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gspn_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from linear_spatial_propagation_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_strings(lib):
+    assert lib.gspn_version() == 1
+    for code in range(0, -11, -1):
+        s = _lib.status_string(code)
+        assert s.startswith("GSPN_"), (code, s)
+    assert "unknown" in _lib.status_string(-99)
+
+
+FAKE = 1 << 40  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def call(**kw):
+    args = dict(x=FAKE, w=FAKE + (1 << 32), lam=FAKE + (2 << 32), u=FAKE + (3 << 32), y=FAKE + (4 << 32),
+                B=2, C=8, H=16, W=16, dirs=15, groups=1, ch_per_weight=1, dtype=1, path=0)
+    args.update(kw)
+    return _lib.scan_fwd_ptr(args["x"], args["w"], args["lam"], args["u"], args["y"], args["B"],
+                             args["C"], args["H"], args["W"], dirs=args["dirs"], groups=args["groups"],
+                             ch_per_weight=args["ch_per_weight"], dtype=args["dtype"], path=args["path"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(C=-1), -2), (dict(H=0), -2), (dict(W=4097), -2), (dict(H=5000), -2),
+    (dict(B=1 << 20, C=1 << 20), -2),
+    (dict(dirs=0), -3), (dict(dirs=16), -3), (dict(dirs=0x1F), -3),
+    (dict(groups=0), -4), (dict(groups=3), -4), (dict(H=12, groups=8, dirs=1), -4),
+    (dict(W=12, groups=8, dirs=4), -4),
+    (dict(ch_per_weight=0), -5), (dict(ch_per_weight=3), -5),
+    (dict(dtype=2), -6), (dict(dtype=-1), -6),
+    (dict(x=0), -1), (dict(w=0), -1), (dict(y=0), -1), (dict(lam=0), -1), (dict(u=0), -1),
+    (dict(x=FAKE + 8), -7), (dict(y=FAKE + (4 << 32) + 2), -7),
+    (dict(y=FAKE), -8), (dict(y=FAKE + (3 << 32) + 64), -8),
+    (dict(path=7), -10), (dict(path=1, H=65), -10),
+])
+def test_invalid_arguments_rejected_on_host(lib, kw, code):
+    assert call(**kw) == code
+
+
+def test_groups_only_checked_on_scanned_sides(lib):
+    # H=12 is not divisible by 8, but only LR/RL scan W=16: the size check
+    # passes, so the call proceeds to the pointer checks (aliasing here)
+    assert call(H=12, W=16, groups=8, dirs=12, y=FAKE) == -8
+
+
+def test_select_path(lib):
+    assert gspn.select_path(32, 128, 64, 64, ch_per_weight=8) == gspn.PATH_FUSED
+    assert gspn.select_path(1, 8, 32, 32) == gspn.PATH_FUSED
+    assert gspn.select_path(8, 256, 128, 128, groups=8) == gspn.PATH_GENERAL
+    assert gspn.select_path(1, 320, 512, 512) == gspn.PATH_GENERAL
+    assert gspn.select_path(1, 8, 32, 32, dirs=0) == -3
+
+
+def test_python_wrapper_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 2, 4, 4)
+    with pytest.raises(ValueError):
+        gspn.scan_fwd(x, torch.zeros(4, 1, 2, 3, 4, 4), x, x)  # CPU tensors
+
+
+def test_check_raises_with_status(lib):
+    with pytest.raises(gspn.GspnError) as ei:
+        _lib.check(-4)
+    assert ei.value.status == -4
