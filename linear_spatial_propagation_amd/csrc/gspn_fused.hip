@@ -17,7 +17,8 @@
 //    adjacent lanes through DPP wave shifts -- no LDS traffic, no barrier in
 //    the recurrence.
 //  * Each wave normalises its direction's taps once per workgroup (3 exp + 1
-//    rcp per pixel) into registers (64 lines x 3 taps) and reuses them for
+//    rcp per pixel) into registers (64 lines x 2 taps; the middle tap is
+//    implied by the unit row sum) and reuses them for
 //    every channel of the weight set: the sigmoid work is shared by the
 //    channel group instead of being repeated per channel.
 //  * lambda * x of the current channel is staged once in LDS as fp32
@@ -116,12 +117,136 @@ __device__ __forceinline__ void store_out(float* __restrict__ p, const float (&v
     }
 }
 
+// ---------------------------------------------------------------- scan
+// One part of one direction's scan of the channel held in X, on lane p.
+//  ASC: lines are visited in increasing line coordinate j (TB: row j, LR:
+//  column j); otherwise decreasing (BT, RL).  STRIDE: floats between
+//  consecutive line coordinates in an LDS plane (65 for rows, 1 for
+//  columns); X and P point at this lane's float at j = 0.  ADD: add h onto
+//  the partner direction's stores instead of storing.  X (and P when
+//  adding) are prefetched kDepth lines ahead.
+//  The middle tap's weight is 1 - w0 - w2 (rows are stochastic), so one
+//  step is h' = (h + xl) + w0 (h[p-1] - h) + w2 (h[p+1] - h): the lane
+//  exchange fuses into the two subtractions (v_sub_f32 with a DPP source)
+//  and only w0 and w2 occupy registers.
+constexpr int kDepth = 4;
+
+__device__ __forceinline__ float line_step(float h, float xl, float w0, float w2) {
+    const float dl = from_left(h) - h;
+    const float dr = from_right(h) - h;
+    float v = h + xl;
+    v = fmaf(w0, dl, v);
+    return fmaf(w2, dr, v);
+}
+
+// Static form: a global scan over exactly kS lines, scan steps [S0, S1).
+template <bool ASC, int STRIDE, bool ADD, int S0, int S1>
+__device__ __forceinline__ void scan_static(const float* __restrict__ X, float* __restrict__ P,
+                                            const float (&w0)[kS], const float (&w2)[kS], float& h) {
+    float xp[kDepth], pp[kDepth];
+#pragma unroll
+    for (int t = 0; t < kDepth; ++t) {
+        const int j = ASC ? S0 + t : kS - 1 - (S0 + t);
+        xp[t] = X[j * STRIDE];
+        if (ADD) pp[t] = P[j * STRIDE];
+    }
+#pragma unroll
+    for (int st = S0; st < S1; ++st) {
+        const int j = ASC ? st : kS - 1 - st;
+        const int slot = (st - S0) % kDepth;
+        const float xl = xp[slot];
+        const float pv = ADD ? pp[slot] : 0.0f;
+        if (st + kDepth < S1) {
+            const int jn = ASC ? j + kDepth : j - kDepth;
+            xp[slot] = X[jn * STRIDE];
+            if (ADD) pp[slot] = P[jn * STRIDE];
+        }
+        h = st == 0 ? xl : line_step(h, xl, w0[j], w2[j]);
+        P[j * STRIDE] = ADD ? pv + h : h;
+    }
+}
+
+// General form: any line count n <= kS and group length L.  The loop is
+// unrolled over all kS line coordinates so the weight registers and LDS
+// offsets stay static; `skip` and `cnt` (uniform) select which of them this
+// part processes and `gpos` is the scan step's position in its group.  They
+// are kept opaque to the optimiser so the per-line conditions are evaluated
+// in the loop with scalar instructions instead of being precomputed.
+template <bool ASC, int STRIDE, bool ADD>
+__device__ __forceinline__ void scan_general(const float* __restrict__ X, float* __restrict__ P,
+                                             const float (&w0)[kS], const float (&w2)[kS], int L,
+                                             int skip, int cnt, int& gpos, float& h) {
+    float xp[kDepth], pp[kDepth];
+#pragma unroll
+    for (int t = 0; t < kDepth; ++t) {
+        const int j = ASC ? t : kS - 1 - t;
+        xp[t] = X[j * STRIDE];
+        if (ADD) pp[t] = P[j * STRIDE];
+    }
+#pragma unroll
+    for (int t = 0; t < kS; ++t) {
+        const int j = ASC ? t : kS - 1 - t;
+        const float xl = xp[t % kDepth];
+        const float pv = ADD ? pp[t % kDepth] : 0.0f;
+        if (t + kDepth < kS) {
+            const int jn = ASC ? j + kDepth : j - kDepth;
+            xp[t % kDepth] = X[jn * STRIDE];
+            if (ADD) pp[t % kDepth] = P[jn * STRIDE];
+        }
+        asm volatile("" : "+s"(skip), "+s"(cnt), "+s"(gpos));
+        if (skip > 0) {
+            --skip;
+        } else if (cnt > 0) {
+            --cnt;
+            h = gpos == 0 ? xl : line_step(h, xl, w0[j], w2[j]);
+            gpos = gpos + 1 == L ? 0 : gpos + 1;
+            P[j * STRIDE] = ADD ? pv + h : h;
+        }
+    }
+}
+
+struct ScanCtl {
+    int d;          // direction 0..3 (TB, BT, LR, RL)
+    int p;          // lane = position on the line
+    bool fast;      // global scan of kS lines with both directions of the pair on
+    int L;          // lines per group
+    int skip1, cnt1, skip2, cnt2;  // general form: store part, add part
+};
+
+template <int D, bool ADD>
+__device__ __forceinline__ void scan_dir(const ScanCtl& k, const float* X, float* P, const float (&w0)[kS],
+                                         const float (&w2)[kS], int& gpos, float& h) {
+    constexpr bool kAsc = (D == 0 || D == 2);
+    constexpr int kStride = D < 2 ? kPitch : 1;
+    const int base = D < 2 ? k.p : k.p * kPitch;
+    if (k.fast) {
+        if (ADD) scan_static<kAsc, kStride, true, kS / 2, kS>(X + base, P + base, w0, w2, h);
+        else scan_static<kAsc, kStride, false, 0, kS / 2>(X + base, P + base, w0, w2, h);
+    } else {
+        scan_general<kAsc, kStride, ADD>(X + base, P + base, w0, w2, k.L, ADD ? k.skip2 : k.skip1,
+                                         ADD ? k.cnt2 : k.cnt1, gpos, h);
+    }
+}
+
+template <bool ADD>
+__device__ __forceinline__ void scan_any(const ScanCtl& k, const float* X, float* P, const float (&w0)[kS],
+                                         const float (&w2)[kS], int& gpos, float& h) {
+    switch (k.d) {
+        case 0: scan_dir<0, ADD>(k, X, P, w0, w2, gpos, h); break;
+        case 1: scan_dir<1, ADD>(k, X, P, w0, w2, gpos, h); break;
+        case 2: scan_dir<2, ADD>(k, X, P, w0, w2, gpos, h); break;
+        default: scan_dir<3, ADD>(k, X, P, w0, w2, gpos, h); break;
+    }
+}
+
+// ---------------------------------------------------------------- kernel
 template <typename T>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fused_scan_kernel(FusedParams prm) {
-    constexpr int N = Vec<T>::N;         // elements per 16-byte access
-    constexpr int kMaxIt = kS * kS / (kThreads * N);
-    __shared__ float lds[4 * kPlane];    // XL[2] | P_row | P_col
+    constexpr int N = Vec<T>::N;                     // elements per 16-byte access
+    constexpr int kMaxIt = kS * kS / (kThreads * N); // merge/staging iterations
+    constexpr bool kPrefetch = sizeof(T) == 2;       // fp32 has no registers to spare
+    __shared__ float lds[4 * kPlane];                // XL[2] | P_row | P_col
 
     const T* __restrict__ gx = static_cast<const T*>(prm.x);
     const T* __restrict__ gw = static_cast<const T*>(prm.w);
@@ -132,6 +257,7 @@ void fused_scan_kernel(FusedParams prm) {
     const int H = prm.H, W = prm.W, B = prm.B, C = prm.C, Cw = prm.Cw;
     const int HW = H * W;
     const uint32_t dirs = prm.dirs;
+    const bool vec = (W % N) == 0;   // rows are whole 16-byte vectors
 
     // ---- which (b, k, chunk) this workgroup owns
     const int wg = blockIdx.x;
@@ -142,11 +268,12 @@ void fused_scan_kernel(FusedParams prm) {
     const int c_begin = k * prm.cpw + chunk * prm.chunk_len;
     const int c_end = min(c_begin + prm.chunk_len, (k + 1) * prm.cpw);
 
-    // ---- this wave's direction
+    // ---- this wave's direction; lane p = position on the line
     const int tid = threadIdx.x;
     const int d = uniform(tid >> 6);
     const int p = tid & 63;
     const bool is_row = d < 2;
+    const bool asc = (d == 0 || d == 2);
     const bool on = (dirs >> d) & 1u;
     const bool partner_on = (dirs >> (d ^ 1)) & 1u;
     const int n = is_row ? H : W;      // lines
@@ -154,61 +281,108 @@ void fused_scan_kernel(FusedParams prm) {
     const int L = n / prm.groups;      // lines per group
     const bool has0 = p >= 1;
     const bool has2 = p + 1 < m;
-    uint64_t start_mask = 0;           // bit s: line s starts a group
-    for (int s = 0; s < n; s += L) start_mask |= 1ull << s;
 
-    // ---- prologue: normalised taps of this direction, one line per step s.
-    // Taps are staged through LDS in chunks of 16 lines for all four
-    // directions, transposed for the column directions so that every wave
-    // then reads its taps as [line][position] rows (conflict-free).  Entries
-    // outside the grid are staged as 0 so idle lanes stay finite.
-    float w0[kS], w1[kS], w2[kS];
+    // ---- prologue: normalised taps of this direction, indexed by line
+    // coordinate j (row for TB/BT, column for LR/RL).  The taps of 16 line
+    // coordinates of every direction are staged in LDS as fp32 [dir][tap]
+    // [j][position] (pitch 65), transposed for LR/RL; every wave then reads
+    // its taps along its lanes.  Entries outside the grid are staged as 0,
+    // which keeps idle lanes finite.
+    float w0[kS], w2[kS];
     {
         constexpr int kChunk = 16;
-        constexpr int kSP = kPitch;                 // staging row pitch (floats)
-        float* S = lds;                             // [4][3][kChunk][kSP]
+        constexpr int kSP = kPitch;
+        float* S = lds;   // [4][3][kChunk][kSP]
+        constexpr int kVPR = kS / N;                         // vectors per 64-wide row
+        constexpr int kPairsPerPass = kThreads / (kChunk * kVPR);
+        constexpr int kPasses = 6 / kPairsPerPass;           // (dir pair, tap) = 2 x 3
+        const T* wsrc[4];
+        for (int dd = 0; dd < 4; ++dd) {
+            const int slab = __builtin_popcount(dirs & ((1u << dd) - 1u));
+            wsrc[dd] = gw + ((size_t)(slab * B + b) * Cw + k) * 3 * (size_t)HW;
+        }
 #pragma unroll
         for (int ch = 0; ch < kS / kChunk; ++ch) {
-            const int s0 = ch * kChunk;
-            for (int dd = 0; dd < 4; ++dd) {
-                if (!((dirs >> dd) & 1u)) continue;
-                const int slab = __builtin_popcount(dirs & ((1u << dd) - 1u));
-                const T* __restrict__ src = gw + ((size_t)(slab * B + b) * Cw + k) * 3 * (size_t)HW;
-                const int nd_ = dd < 2 ? H : W;
-                const int md_ = dd < 2 ? W : H;
-                float* Sd = S + dd * 3 * kChunk * kSP;
-                if (dd < 2) {
-                    // lines are memory rows: threads run along the row
-                    const int pp = tid & 63;
-                    for (int ii = tid >> 6; ii < kChunk; ii += kThreads / 64) {
-                        const int s = s0 + ii;
-                        const bool ok = s < nd_ && pp < md_;
-                        const int r = dd == 0 ? s : H - 1 - s;
-                        for (int t = 0; t < 3; ++t)
-                            Sd[(t * kChunk + ii) * kSP + pp] = ok ? to_f32(src[(size_t)t * HW + r * W + pp]) : 0.0f;
+            const int j0 = ch * kChunk;
+            if (vec) {
+                // 16-byte loads, all issued before the LDS writes.
+                // rows (TB, BT): thread -> (jj, vector pv along the row)
+                // columns (LR, RL): thread -> (row r, vector along the 16 columns)
+                uint4 rv[2][kPasses];
+                bool rok[2][kPasses];
+#pragma unroll
+                for (int grp = 0; grp < 2; ++grp) {
+#pragma unroll
+                    for (int ps = 0; ps < kPasses; ++ps) {
+                        const int pair = ps * kPairsPerPass + tid / (kChunk * kVPR);   // 0..5
+                        const int dd = grp * 2 + pair / 3;
+                        const int t = pair % 3;
+                        const int e = tid % (kChunk * kVPR);
+                        int r, c;
+                        if (grp == 0) { r = j0 + e / kVPR; c = (e % kVPR) * N; }
+                        else { r = e / (kChunk / N); c = j0 + (e % (kChunk / N)) * N; }
+                        const bool ok = ((dirs >> dd) & 1u) && r < H && c + N <= W;
+                        rok[grp][ps] = ok;
+                        rv[grp][ps] = ok ? *reinterpret_cast<const uint4*>(wsrc[dd] + (size_t)t * HW + r * W + c)
+                                         : make_uint4(0u, 0u, 0u, 0u);
                     }
-                } else {
-                    // lines are memory columns: threads run along the row
-                    // (across lines) and the tile is written transposed
-                    const int ii = tid & (kChunk - 1);
-                    const int s = s0 + ii;
-                    const int q = dd == 2 ? s : W - 1 - s;
-                    for (int pp = tid / kChunk; pp < kS; pp += kThreads / kChunk) {
-                        const bool ok = s < nd_ && pp < md_;
-                        for (int t = 0; t < 3; ++t)
-                            Sd[(t * kChunk + ii) * kSP + pp] = ok ? to_f32(src[(size_t)t * HW + pp * W + q]) : 0.0f;
+                }
+#pragma unroll
+                for (int grp = 0; grp < 2; ++grp) {
+#pragma unroll
+                    for (int ps = 0; ps < kPasses; ++ps) {
+                        const int pair = ps * kPairsPerPass + tid / (kChunk * kVPR);
+                        const int dd = grp * 2 + pair / 3;
+                        const int t = pair % 3;
+                        const int e = tid % (kChunk * kVPR);
+                        float f[N];
+                        unpack(rv[grp][ps], f);
+                        float* Sd = S + (dd * 3 + t) * kChunk * kSP;
+                        if (grp == 0) {
+                            const int jj = e / kVPR, c = (e % kVPR) * N;
+#pragma unroll
+                            for (int q = 0; q < N; ++q) Sd[jj * kSP + c + q] = f[q];
+                        } else {
+                            const int r = e / (kChunk / N), jj0 = (e % (kChunk / N)) * N;
+#pragma unroll
+                            for (int q = 0; q < N; ++q) Sd[(jj0 + q) * kSP + r] = f[q];
+                        }
+                    }
+                }
+            } else {
+                // element loads (rows that are not whole 16-byte vectors)
+                for (int dd = 0; dd < 4; ++dd) {
+                    if (!((dirs >> dd) & 1u)) continue;
+                    float* Sd = S + dd * 3 * kChunk * kSP;
+                    if (dd < 2) {
+                        const int pp = tid & 63;
+                        for (int jj = tid >> 6; jj < kChunk; jj += kThreads / 64) {
+                            const int r = j0 + jj;
+                            const bool ok = r < H && pp < W;
+                            for (int t = 0; t < 3; ++t)
+                                Sd[(t * kChunk + jj) * kSP + pp] =
+                                    ok ? to_f32(wsrc[dd][(size_t)t * HW + r * W + pp]) : 0.0f;
+                        }
+                    } else {
+                        const int jj = tid & (kChunk - 1);
+                        const int q = j0 + jj;
+                        for (int pp = tid / kChunk; pp < kS; pp += kThreads / kChunk) {
+                            const bool ok = q < W && pp < H;
+                            for (int t = 0; t < 3; ++t)
+                                Sd[(t * kChunk + jj) * kSP + pp] =
+                                    ok ? to_f32(wsrc[dd][(size_t)t * HW + pp * W + q]) : 0.0f;
+                        }
                     }
                 }
             }
             __syncthreads();
             const float* Sw = S + d * 3 * kChunk * kSP + p;
 #pragma unroll
-            for (int ii = 0; ii < kChunk; ++ii) {
-                const Taps tp = normalise_taps(Sw[ii * kSP], Sw[(kChunk + ii) * kSP],
-                                               Sw[(2 * kChunk + ii) * kSP], has0, has2);
-                w0[s0 + ii] = tp.w0;
-                w1[s0 + ii] = tp.w1;
-                w2[s0 + ii] = tp.w2;
+            for (int jj = 0; jj < kChunk; ++jj) {
+                const Taps tp = normalise_taps(Sw[jj * kSP], Sw[(kChunk + jj) * kSP],
+                                               Sw[(2 * kChunk + jj) * kSP], has0, has2);
+                w0[j0 + jj] = tp.w0;
+                w2[j0 + jj] = tp.w2;
             }
             __syncthreads();
         }
@@ -222,7 +396,6 @@ void fused_scan_kernel(FusedParams prm) {
     const int col0 = tc * N;
     const int nvalid = min(N, W - col0);
     const bool t_active = tr < rpi;
-    const bool vec = (W % N) == 0;
     const bool row_any = (dirs & 3u) != 0;
     const bool col_any = (dirs & 12u) != 0;
 
@@ -233,16 +406,13 @@ void fused_scan_kernel(FusedParams prm) {
     }
     __syncthreads();
 
-    uint4 xr[kMaxIt], lr[kMaxIt];
-    auto load_xl = [&](int c) {
+    uint4 xr[kMaxIt], lr[kMaxIt], ur[kMaxIt];
+    auto load_rows = [&](const T* __restrict__ g, int c, uint4 (&dst)[kMaxIt]) {
         const size_t base = ((size_t)b * C + c) * (size_t)HW;
 #pragma unroll
         for (int it = 0; it < kMaxIt; ++it) {
             const int r = tr + it * rpi;
-            if (t_active && r < H) {
-                xr[it] = load_raw(gx + base + r * W + col0, nvalid, vec);
-                lr[it] = load_raw(glam + base + r * W + col0, nvalid, vec);
-            }
+            if (t_active && r < H) dst[it] = load_raw(g + base + r * W + col0, nvalid, vec);
         }
     };
     auto write_xl = [&](float* X) {
@@ -253,77 +423,64 @@ void fused_scan_kernel(FusedParams prm) {
                 float xv[N], lv[N];
                 unpack(xr[it], xv);
                 unpack(lr[it], lv);
+                if (vec) {
 #pragma unroll
-                for (int j = 0; j < N; ++j)
-                    if (j < nvalid) X[r * kPitch + col0 + j] = xv[j] * lv[j];
+                    for (int j = 0; j < N; ++j) X[r * kPitch + col0 + j] = xv[j] * lv[j];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < N; ++j)
+                        if (j < nvalid) X[r * kPitch + col0 + j] = xv[j] * lv[j];
+                }
             }
         }
     };
 
-    load_xl(c_begin);
+    load_rows(gx, c_begin, xr);
+    load_rows(glam, c_begin, lr);
     write_xl(lds);
     __syncthreads();
 
     float* const Pl = lds + (is_row ? 2 : 3) * kPlane;
     const int nstore = partner_on ? ((d & 1) ? n / 2 : (n + 1) / 2) : n;
-    int off0, delta;
-    switch (d) {
-        case 0: off0 = p; delta = kPitch; break;                    // TB
-        case 1: off0 = (H - 1) * kPitch + p; delta = -kPitch; break;  // BT
-        case 2: off0 = p * kPitch; delta = 1; break;                // LR
-        default: off0 = p * kPitch + W - 1; delta = -1; break;      // RL
-    }
+    ScanCtl ctl;
+    ctl.d = d;
+    ctl.p = p;
+    ctl.fast = n == kS && L == kS && partner_on;
+    ctl.L = L;
+    ctl.skip1 = asc ? 0 : kS - n;          // general form: first visited
+    ctl.cnt1 = nstore;                     // line coordinate is 0 (asc)
+    ctl.skip2 = ctl.skip1 + nstore;        // or n-1 (desc)
+    ctl.cnt2 = n - nstore;
 
     for (int c = c_begin; c < c_end; ++c) {
         const int buf = (c - c_begin) & 1;
         const float* const X = lds + buf * kPlane;
         const bool has_next = c + 1 < c_end;
-        if (has_next) load_xl(c + 1);
+        if (kPrefetch) {
+            load_rows(gu, c, ur);
+            if (has_next) {
+                load_rows(gx, c + 1, xr);
+                load_rows(glam, c + 1, lr);
+            }
+        }
 
-        // ---- scan: first part stores, second part adds onto the partner
+        // ---- scan: the first part stores, the second adds onto the partner
         float h = 0.0f;
-        int off = off0;
-        if (on) {
-#pragma unroll
-            for (int s = 0; s < kS; ++s) {
-                if (s < nstore) {
-                    const float xl = X[off];
-                    if ((start_mask >> s) & 1u) {
-                        h = xl;
-                    } else {
-                        const float hl = from_left(h), hr = from_right(h);
-                        float v = fmaf(w1[s], h, xl);
-                        v = fmaf(w0[s], hl, v);
-                        h = fmaf(w2[s], hr, v);
-                    }
-                    Pl[off] = h;
-                    off += delta;
-                }
-            }
-        }
+        int gpos = 0;
+        if (on) scan_any<false>(ctl, X, Pl, w0, w2, gpos, h);
         __syncthreads();
-        if (on) {
-#pragma unroll
-            for (int s = 0; s < kS; ++s) {
-                if (s >= nstore && s < n) {
-                    const float xl = X[off];
-                    if ((start_mask >> s) & 1u) {
-                        h = xl;
-                    } else {
-                        const float hl = from_left(h), hr = from_right(h);
-                        float v = fmaf(w1[s], h, xl);
-                        v = fmaf(w0[s], hl, v);
-                        h = fmaf(w2[s], hr, v);
-                    }
-                    Pl[off] += h;
-                    off += delta;
-                }
+        if (on) scan_any<true>(ctl, X, Pl, w0, w2, gpos, h);
+        if (has_next) {
+            if (!kPrefetch) {
+                load_rows(gx, c + 1, xr);
+                load_rows(glam, c + 1, lr);
             }
+            write_xl(lds + (buf ^ 1) * kPlane);
         }
-        if (has_next) write_xl(lds + (buf ^ 1) * kPlane);
+        if (!kPrefetch) load_rows(gu, c, ur);
         __syncthreads();
 
-        // ---- merge: y = u * (P_row + P_col)
+        // ---- merge: y = u * (P_row + P_col), rounded to the I/O dtype
         {
             const size_t base = ((size_t)b * C + c) * (size_t)HW;
             const float* PR = lds + 2 * kPlane;
@@ -333,12 +490,12 @@ void fused_scan_kernel(FusedParams prm) {
                 const int r = tr + it * rpi;
                 if (t_active && r < H) {
                     float uv[N], yv[N];
-                    unpack(load_raw(gu + base + r * W + col0, nvalid, vec), uv);
+                    unpack(ur[it], uv);
 #pragma unroll
                     for (int j = 0; j < N; ++j) {
                         const int o = r * kPitch + col0 + j;
                         float acc = 0.0f;
-                        if (j < nvalid) {
+                        if (vec || j < nvalid) {
                             if (row_any) acc = PR[o];
                             if (col_any) acc += PC[o];
                         }
