@@ -41,7 +41,8 @@ namespace gspn {
 namespace {
 
 constexpr int kS = kFusedMaxSide;    // max lines and max positions
-constexpr int kPitch = kS + 1;       // LDS row pitch (floats) of a 64 x 64 plane
+constexpr int kPitch = kS + 4;       // LDS row pitch (floats): rows 16-byte aligned; row
+                                     // and 4-wide column accesses are conflict-free
 constexpr int kPlane = kS * kPitch;  // floats per LDS plane
 constexpr int kThreads = 256;
 
@@ -128,7 +129,7 @@ __device__ __forceinline__ void store_out(float* __restrict__ p, const float (&v
 //  The middle tap's weight is 1 - w0 - w2 (rows are stochastic), so one
 //  step is h' = (h + xl) + w0 (h[p-1] - h) + w2 (h[p+1] - h): the lane
 //  exchange fuses into the two subtractions (v_sub_f32 with a DPP source)
-//  and only w0 and w2 occupy registers.
+//  and only w0 and w2 occupy registers (64 lines x 2 per lane).
 constexpr int kDepth = 4;
 
 __device__ __forceinline__ float line_step(float h, float xl, float w0, float w2) {
@@ -164,6 +165,45 @@ __device__ __forceinline__ void scan_static(const float* __restrict__ X, float* 
         h = st == 0 ? xl : line_step(h, xl, w0[j], w2[j]);
         P[j * STRIDE] = ADD ? pv + h : h;
     }
+}
+
+// Static form for column directions (stride 1): the line coordinates of a
+// lane are contiguous, so X and P move 4 lines per 16-byte LDS access; the
+// next block is read while the current one is scanned.
+template <bool ASC, bool ADD, int S0, int S1>
+__device__ __forceinline__ void scan_static_cols(const float* __restrict__ X, float* __restrict__ P,
+                                                 const float (&w0)[kS], const float (&w2)[kS],
+                                                 float& h) {
+    static_assert(S0 % 4 == 0 && S1 % 4 == 0, "blocks of 4 lines");
+    constexpr int kBlocks = (S1 - S0) / 4;
+    const float4* X4 = reinterpret_cast<const float4*>(X);
+    float4* P4 = reinterpret_cast<float4*>(P);
+    // block of the i-th group of 4 scan steps
+#define GSPN_BLK(i) (ASC ? (S0 / 4 + (i)) : (kS / 4 - 1 - (S0 / 4 + (i))))
+    float4 xc = X4[GSPN_BLK(0)], xn = xc;
+    float4 pc = ADD ? P4[GSPN_BLK(0)] : xc, pn = pc;
+#pragma unroll
+    for (int i = 0; i < kBlocks; ++i) {
+        if (i + 1 < kBlocks) {
+            xn = X4[GSPN_BLK(i + 1)];
+            if (ADD) pn = P4[GSPN_BLK(i + 1)];
+        }
+        const float xs[4] = {xc.x, xc.y, xc.z, xc.w};
+        const float ps[4] = {pc.x, pc.y, pc.z, pc.w};
+        float hs[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = ASC ? q : 3 - q;          // element of the block, in scan order
+            const int st = S0 + 4 * i + q;          // scan step
+            const int j = GSPN_BLK(i) * 4 + e;      // line coordinate
+            h = st == 0 ? xs[e] : line_step(h, xs[e], w0[j], w2[j]);
+            hs[e] = ADD ? ps[e] + h : h;
+        }
+        P4[GSPN_BLK(i)] = make_float4(hs[0], hs[1], hs[2], hs[3]);
+        xc = xn;
+        pc = pn;
+    }
+#undef GSPN_BLK
 }
 
 // General form: any line count n <= kS and group length L.  The loop is
@@ -220,8 +260,13 @@ __device__ __forceinline__ void scan_dir(const ScanCtl& k, const float* X, float
     constexpr int kStride = D < 2 ? kPitch : 1;
     const int base = D < 2 ? k.p : k.p * kPitch;
     if (k.fast) {
-        if (ADD) scan_static<kAsc, kStride, true, kS / 2, kS>(X + base, P + base, w0, w2, h);
-        else scan_static<kAsc, kStride, false, 0, kS / 2>(X + base, P + base, w0, w2, h);
+        if (D >= 2) {
+            if (ADD) scan_static_cols<kAsc, true, kS / 2, kS>(X + base, P + base, w0, w2, h);
+            else scan_static_cols<kAsc, false, 0, kS / 2>(X + base, P + base, w0, w2, h);
+        } else {
+            if (ADD) scan_static<kAsc, kStride, true, kS / 2, kS>(X + base, P + base, w0, w2, h);
+            else scan_static<kAsc, kStride, false, 0, kS / 2>(X + base, P + base, w0, w2, h);
+        }
     } else {
         scan_general<kAsc, kStride, ADD>(X + base, P + base, w0, w2, k.L, ADD ? k.skip2 : k.skip1,
                                          ADD ? k.cnt2 : k.cnt1, gpos, h);
@@ -239,14 +284,104 @@ __device__ __forceinline__ void scan_any(const ScanCtl& k, const float* X, float
     }
 }
 
+// ---------------------------------------------------------------- staging
+// Raw taps of 16 line coordinates [j0, j0+16) of all four directions,
+// loaded as 16-byte vectors (rows that are whole vectors only).  Row
+// directions: thread -> (line jj, vector along the row); column directions:
+// thread -> (row r, vector along the 16 columns).
+template <typename T>
+struct TapChunk {
+    static constexpr int N = Vec<T>::N;
+    static constexpr int kChunk = 16;
+    static constexpr int kVPR = kS / N;                           // vectors per 64-wide row
+    static constexpr int kPairsPerPass = kThreads / (kChunk * kVPR);
+    static constexpr int kPasses = 6 / kPairsPerPass;             // (dir pair, tap) = 2 x 3
+    uint4 v[2][kPasses];
+
+    __device__ __forceinline__ void load(const T* const (&wsrc)[4], uint32_t dirs, int j0, int H, int W,
+                                         int HW, int tid) {
+#pragma unroll
+        for (int grp = 0; grp < 2; ++grp) {
+#pragma unroll
+            for (int ps = 0; ps < kPasses; ++ps) {
+                const int pair = ps * kPairsPerPass + tid / (kChunk * kVPR);   // 0..5
+                const int dd = grp * 2 + pair / 3;
+                const int t = pair % 3;
+                const int e = tid % (kChunk * kVPR);
+                int r, c;
+                if (grp == 0) { r = j0 + e / kVPR; c = (e % kVPR) * N; }
+                else { r = e / (kChunk / N); c = j0 + (e % (kChunk / N)) * N; }
+                const bool ok = ((dirs >> dd) & 1u) && r < H && c + N <= W;
+                v[grp][ps] = ok ? *reinterpret_cast<const uint4*>(wsrc[dd] + (size_t)t * HW + r * W + c)
+                                : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    }
+    // Write as fp32 into S[dir][tap][jj][position] (pitch kPitch).
+    __device__ __forceinline__ void store(float* S, int tid) const {
+#pragma unroll
+        for (int grp = 0; grp < 2; ++grp) {
+#pragma unroll
+            for (int ps = 0; ps < kPasses; ++ps) {
+                const int pair = ps * kPairsPerPass + tid / (kChunk * kVPR);
+                const int dd = grp * 2 + pair / 3;
+                const int t = pair % 3;
+                const int e = tid % (kChunk * kVPR);
+                float f[N];
+                unpack(v[grp][ps], f);
+                float* Sd = S + (dd * 3 + t) * kChunk * kPitch;
+                if (grp == 0) {
+                    const int jj = e / kVPR, c = (e % kVPR) * N;
+#pragma unroll
+                    for (int q = 0; q < N; ++q) Sd[jj * kPitch + c + q] = f[q];
+                } else {
+                    const int r = e / (kChunk / N), jj0 = (e % (kChunk / N)) * N;
+#pragma unroll
+                    for (int q = 0; q < N; ++q) Sd[(jj0 + q) * kPitch + r] = f[q];
+                }
+            }
+        }
+    }
+};
+
+// Element-wise staging of the same chunk (rows that are not whole vectors).
+template <typename T>
+__device__ __forceinline__ void stage_taps_scalar(float* S, const T* const (&wsrc)[4], uint32_t dirs, int j0,
+                                                  int H, int W, int HW, int tid) {
+    constexpr int kChunk = 16;
+    for (int dd = 0; dd < 4; ++dd) {
+        if (!((dirs >> dd) & 1u)) continue;
+        float* Sd = S + dd * 3 * kChunk * kPitch;
+        if (dd < 2) {
+            const int pp = tid & 63;
+            for (int jj = tid >> 6; jj < kChunk; jj += kThreads / 64) {
+                const int r = j0 + jj;
+                const bool ok = r < H && pp < W;
+                for (int t = 0; t < 3; ++t)
+                    Sd[(t * kChunk + jj) * kPitch + pp] = ok ? to_f32(wsrc[dd][(size_t)t * HW + r * W + pp]) : 0.0f;
+            }
+        } else {
+            const int jj = tid & (kChunk - 1);
+            const int q = j0 + jj;
+            for (int pp = tid / kChunk; pp < kS; pp += kThreads / kChunk) {
+                const bool ok = q < W && pp < H;
+                for (int t = 0; t < 3; ++t)
+                    Sd[(t * kChunk + jj) * kPitch + pp] = ok ? to_f32(wsrc[dd][(size_t)t * HW + pp * W + q]) : 0.0f;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- kernel
 template <typename T>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fused_scan_kernel(FusedParams prm) {
     constexpr int N = Vec<T>::N;                     // elements per 16-byte access
     constexpr int kMaxIt = kS * kS / (kThreads * N); // merge/staging iterations
-    constexpr bool kPrefetch = sizeof(T) == 2;       // fp32 has no registers to spare
-    __shared__ float lds[4 * kPlane];                // XL[2] | P_row | P_col
+    constexpr int kChunk = 16;
+    // LDS: XL (lambda*x of the current channel, fp32) | P_row | P_col; the
+    // tap staging of the prologue reuses the same space.
+    __shared__ __attribute__((aligned(16))) float lds[3 * kPlane];
 
     const T* __restrict__ gx = static_cast<const T*>(prm.x);
     const T* __restrict__ gw = static_cast<const T*>(prm.w);
@@ -257,7 +392,7 @@ void fused_scan_kernel(FusedParams prm) {
     const int H = prm.H, W = prm.W, B = prm.B, C = prm.C, Cw = prm.Cw;
     const int HW = H * W;
     const uint32_t dirs = prm.dirs;
-    const bool vec = (W % N) == 0;   // rows are whole 16-byte vectors
+    const bool vec = (W % N) == 0;                 // rows are whole 16-byte vectors
 
     // ---- which (b, k, chunk) this workgroup owns
     const int wg = blockIdx.x;
@@ -282,113 +417,7 @@ void fused_scan_kernel(FusedParams prm) {
     const bool has0 = p >= 1;
     const bool has2 = p + 1 < m;
 
-    // ---- prologue: normalised taps of this direction, indexed by line
-    // coordinate j (row for TB/BT, column for LR/RL).  The taps of 16 line
-    // coordinates of every direction are staged in LDS as fp32 [dir][tap]
-    // [j][position] (pitch 65), transposed for LR/RL; every wave then reads
-    // its taps along its lanes.  Entries outside the grid are staged as 0,
-    // which keeps idle lanes finite.
-    float w0[kS], w2[kS];
-    {
-        constexpr int kChunk = 16;
-        constexpr int kSP = kPitch;
-        float* S = lds;   // [4][3][kChunk][kSP]
-        constexpr int kVPR = kS / N;                         // vectors per 64-wide row
-        constexpr int kPairsPerPass = kThreads / (kChunk * kVPR);
-        constexpr int kPasses = 6 / kPairsPerPass;           // (dir pair, tap) = 2 x 3
-        const T* wsrc[4];
-        for (int dd = 0; dd < 4; ++dd) {
-            const int slab = __builtin_popcount(dirs & ((1u << dd) - 1u));
-            wsrc[dd] = gw + ((size_t)(slab * B + b) * Cw + k) * 3 * (size_t)HW;
-        }
-#pragma unroll
-        for (int ch = 0; ch < kS / kChunk; ++ch) {
-            const int j0 = ch * kChunk;
-            if (vec) {
-                // 16-byte loads, all issued before the LDS writes.
-                // rows (TB, BT): thread -> (jj, vector pv along the row)
-                // columns (LR, RL): thread -> (row r, vector along the 16 columns)
-                uint4 rv[2][kPasses];
-                bool rok[2][kPasses];
-#pragma unroll
-                for (int grp = 0; grp < 2; ++grp) {
-#pragma unroll
-                    for (int ps = 0; ps < kPasses; ++ps) {
-                        const int pair = ps * kPairsPerPass + tid / (kChunk * kVPR);   // 0..5
-                        const int dd = grp * 2 + pair / 3;
-                        const int t = pair % 3;
-                        const int e = tid % (kChunk * kVPR);
-                        int r, c;
-                        if (grp == 0) { r = j0 + e / kVPR; c = (e % kVPR) * N; }
-                        else { r = e / (kChunk / N); c = j0 + (e % (kChunk / N)) * N; }
-                        const bool ok = ((dirs >> dd) & 1u) && r < H && c + N <= W;
-                        rok[grp][ps] = ok;
-                        rv[grp][ps] = ok ? *reinterpret_cast<const uint4*>(wsrc[dd] + (size_t)t * HW + r * W + c)
-                                         : make_uint4(0u, 0u, 0u, 0u);
-                    }
-                }
-#pragma unroll
-                for (int grp = 0; grp < 2; ++grp) {
-#pragma unroll
-                    for (int ps = 0; ps < kPasses; ++ps) {
-                        const int pair = ps * kPairsPerPass + tid / (kChunk * kVPR);
-                        const int dd = grp * 2 + pair / 3;
-                        const int t = pair % 3;
-                        const int e = tid % (kChunk * kVPR);
-                        float f[N];
-                        unpack(rv[grp][ps], f);
-                        float* Sd = S + (dd * 3 + t) * kChunk * kSP;
-                        if (grp == 0) {
-                            const int jj = e / kVPR, c = (e % kVPR) * N;
-#pragma unroll
-                            for (int q = 0; q < N; ++q) Sd[jj * kSP + c + q] = f[q];
-                        } else {
-                            const int r = e / (kChunk / N), jj0 = (e % (kChunk / N)) * N;
-#pragma unroll
-                            for (int q = 0; q < N; ++q) Sd[(jj0 + q) * kSP + r] = f[q];
-                        }
-                    }
-                }
-            } else {
-                // element loads (rows that are not whole 16-byte vectors)
-                for (int dd = 0; dd < 4; ++dd) {
-                    if (!((dirs >> dd) & 1u)) continue;
-                    float* Sd = S + dd * 3 * kChunk * kSP;
-                    if (dd < 2) {
-                        const int pp = tid & 63;
-                        for (int jj = tid >> 6; jj < kChunk; jj += kThreads / 64) {
-                            const int r = j0 + jj;
-                            const bool ok = r < H && pp < W;
-                            for (int t = 0; t < 3; ++t)
-                                Sd[(t * kChunk + jj) * kSP + pp] =
-                                    ok ? to_f32(wsrc[dd][(size_t)t * HW + r * W + pp]) : 0.0f;
-                        }
-                    } else {
-                        const int jj = tid & (kChunk - 1);
-                        const int q = j0 + jj;
-                        for (int pp = tid / kChunk; pp < kS; pp += kThreads / kChunk) {
-                            const bool ok = q < W && pp < H;
-                            for (int t = 0; t < 3; ++t)
-                                Sd[(t * kChunk + jj) * kSP + pp] =
-                                    ok ? to_f32(wsrc[dd][(size_t)t * HW + pp * W + q]) : 0.0f;
-                        }
-                    }
-                }
-            }
-            __syncthreads();
-            const float* Sw = S + d * 3 * kChunk * kSP + p;
-#pragma unroll
-            for (int jj = 0; jj < kChunk; ++jj) {
-                const Taps tp = normalise_taps(Sw[jj * kSP], Sw[(kChunk + jj) * kSP],
-                                               Sw[(2 * kChunk + jj) * kSP], has0, has2);
-                w0[j0 + jj] = tp.w0;
-                w2[j0 + jj] = tp.w2;
-            }
-            __syncthreads();
-        }
-    }
-
-    // ---- staging / merge thread mapping: rows of W, N elements per thread
+    // ---- x / lambda / u rows: N elements per thread
     const int tpr = (W + N - 1) / N;         // threads per row
     const int rpi = kThreads / tpr;          // rows per iteration
     const int tr = tid / tpr;
@@ -398,49 +427,94 @@ void fused_scan_kernel(FusedParams prm) {
     const bool t_active = tr < rpi;
     const bool row_any = (dirs & 3u) != 0;
     const bool col_any = (dirs & 12u) != 0;
-
-    // padding rows/columns of XL must read as zero
-    {
-        float4* z = reinterpret_cast<float4*>(lds);
-        for (int i = tid; i < (2 * kPlane) / 4; i += kThreads) z[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    __syncthreads();
-
-    uint4 xr[kMaxIt], lr[kMaxIt], ur[kMaxIt];
     auto load_rows = [&](const T* __restrict__ g, int c, uint4 (&dst)[kMaxIt]) {
-        const size_t base = ((size_t)b * C + c) * (size_t)HW;
+        const T* __restrict__ sl = g + ((size_t)b * C + c) * (size_t)HW;
 #pragma unroll
         for (int it = 0; it < kMaxIt; ++it) {
             const int r = tr + it * rpi;
-            if (t_active && r < H) dst[it] = load_raw(g + base + r * W + col0, nvalid, vec);
+            if (t_active && r < H) dst[it] = load_raw(sl + r * W + col0, nvalid, vec);
         }
     };
-    auto write_xl = [&](float* X) {
+    // XL <- lambda * x (fp32, pitch kPitch)
+    auto write_xl = [&](const uint4 (&xs)[kMaxIt], const uint4 (&ls)[kMaxIt]) {
 #pragma unroll
         for (int it = 0; it < kMaxIt; ++it) {
             const int r = tr + it * rpi;
             if (t_active && r < H) {
                 float xv[N], lv[N];
-                unpack(xr[it], xv);
-                unpack(lr[it], lv);
+                unpack(xs[it], xv);
+                unpack(ls[it], lv);
                 if (vec) {
+                    float4* dst = reinterpret_cast<float4*>(lds + r * kPitch + col0);
 #pragma unroll
-                    for (int j = 0; j < N; ++j) X[r * kPitch + col0 + j] = xv[j] * lv[j];
+                    for (int j = 0; j < N; j += 4)
+                        dst[j / 4] = make_float4(xv[j] * lv[j], xv[j + 1] * lv[j + 1], xv[j + 2] * lv[j + 2],
+                                                 xv[j + 3] * lv[j + 3]);
                 } else {
 #pragma unroll
                     for (int j = 0; j < N; ++j)
-                        if (j < nvalid) X[r * kPitch + col0 + j] = xv[j] * lv[j];
+                        if (j < nvalid) lds[r * kPitch + col0 + j] = xv[j] * lv[j];
                 }
             }
         }
     };
 
-    load_rows(gx, c_begin, xr);
-    load_rows(glam, c_begin, lr);
-    write_xl(lds);
+    // x / lambda of the next channel and u of the current one travel in
+    // registers; the first channel's loads are in flight during the prologue
+    uint4 x1[kMaxIt], l1[kMaxIt], u0[kMaxIt];
+    load_rows(gx, c_begin, x1);
+    load_rows(glam, c_begin, l1);
+    load_rows(gu, c_begin, u0);
+
+    // ---- prologue: normalised taps of this direction, indexed by line
+    // coordinate j (row for TB/BT, column for LR/RL).  The taps of 16 line
+    // coordinates of every direction are staged in LDS as fp32 [dir][tap]
+    // [j][position] (pitch kPitch), transposed for LR/RL; every wave then
+    // reads its taps along its lanes.  The next chunk's loads are in flight
+    // while the current chunk is normalised.  Entries outside the grid are
+    // staged as 0, which keeps idle lanes finite.
+    float w0[kS], w2[kS];
+    {
+        float* S = lds;   // [4][3][kChunk][kPitch]
+        const T* wsrc[4];
+        for (int dd = 0; dd < 4; ++dd) {
+            const int slab = __builtin_popcount(dirs & ((1u << dd) - 1u));
+            wsrc[dd] = gw + ((size_t)(slab * B + b) * Cw + k) * 3 * (size_t)HW;
+        }
+        TapChunk<T> tapv;
+        if (vec) tapv.load(wsrc, dirs, 0, H, W, HW, tid);
+#pragma unroll
+        for (int ch = 0; ch < kS / kChunk; ++ch) {
+            const int j0 = ch * kChunk;
+            if (vec) {
+                tapv.store(S, tid);
+                if (ch + 1 < kS / kChunk) tapv.load(wsrc, dirs, j0 + kChunk, H, W, HW, tid);
+            } else {
+                stage_taps_scalar<T>(S, wsrc, dirs, j0, H, W, HW, tid);
+            }
+            __syncthreads();
+            const float* Sw = S + d * 3 * kChunk * kPitch + p;
+#pragma unroll
+            for (int jj = 0; jj < kChunk; ++jj) {
+                const Taps tp = normalise_taps(Sw[jj * kPitch], Sw[(kChunk + jj) * kPitch],
+                                               Sw[(2 * kChunk + jj) * kPitch], has0, has2);
+                w0[j0 + jj] = tp.w0;
+                w2[j0 + jj] = tp.w2;
+            }
+            __syncthreads();
+        }
+    }
+
+    // padding rows/columns of XL must read as zero
+    {
+        float4* z = reinterpret_cast<float4*>(lds);
+        for (int i = tid; i < kPlane / 4; i += kThreads) z[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+    write_xl(x1, l1);
     __syncthreads();
 
-    float* const Pl = lds + (is_row ? 2 : 3) * kPlane;
+    float* const Pl = lds + (is_row ? 1 : 2) * kPlane;
     const int nstore = partner_on ? ((d & 1) ? n / 2 : (n + 1) / 2) : n;
     ScanCtl ctl;
     ctl.d = d;
@@ -453,57 +527,68 @@ void fused_scan_kernel(FusedParams prm) {
     ctl.cnt2 = n - nstore;
 
     for (int c = c_begin; c < c_end; ++c) {
-        const int buf = (c - c_begin) & 1;
-        const float* const X = lds + buf * kPlane;
         const bool has_next = c + 1 < c_end;
-        if (kPrefetch) {
-            load_rows(gu, c, ur);
-            if (has_next) {
-                load_rows(gx, c + 1, xr);
-                load_rows(glam, c + 1, lr);
-            }
+        if (has_next) {
+            load_rows(gx, c + 1, x1);
+            load_rows(glam, c + 1, l1);
         }
 
         // ---- scan: the first part stores, the second adds onto the partner
         float h = 0.0f;
         int gpos = 0;
-        if (on) scan_any<false>(ctl, X, Pl, w0, w2, gpos, h);
+        if (on) scan_any<false>(ctl, lds, Pl, w0, w2, gpos, h);
         __syncthreads();
-        if (on) scan_any<true>(ctl, X, Pl, w0, w2, gpos, h);
-        if (has_next) {
-            if (!kPrefetch) {
-                load_rows(gx, c + 1, xr);
-                load_rows(glam, c + 1, lr);
-            }
-            write_xl(lds + (buf ^ 1) * kPlane);
-        }
-        if (!kPrefetch) load_rows(gu, c, ur);
+        if (on) scan_any<true>(ctl, lds, Pl, w0, w2, gpos, h);
         __syncthreads();
 
-        // ---- merge: y = u * (P_row + P_col), rounded to the I/O dtype
+        // ---- merge: y = u * (P_row + P_col); then XL <- next channel
         {
-            const size_t base = ((size_t)b * C + c) * (size_t)HW;
-            const float* PR = lds + 2 * kPlane;
-            const float* PC = lds + 3 * kPlane;
+            T* __restrict__ ys = gy + ((size_t)b * C + c) * (size_t)HW;
+            const float* PR = lds + kPlane;
+            const float* PC = lds + 2 * kPlane;
+            if (vec && row_any && col_any) {
 #pragma unroll
-            for (int it = 0; it < kMaxIt; ++it) {
-                const int r = tr + it * rpi;
-                if (t_active && r < H) {
+                for (int it = 0; it < kMaxIt; ++it) {
+                    const int r = tr + it * rpi;
+                    const int o = min(r, H - 1) * kPitch + col0;   // rows past H are read, not stored
                     float uv[N], yv[N];
-                    unpack(ur[it], uv);
+                    unpack(u0[it], uv);
 #pragma unroll
-                    for (int j = 0; j < N; ++j) {
-                        const int o = r * kPitch + col0 + j;
-                        float acc = 0.0f;
-                        if (vec || j < nvalid) {
-                            if (row_any) acc = PR[o];
-                            if (col_any) acc += PC[o];
-                        }
-                        yv[j] = uv[j] * acc;
+                    for (int j = 0; j < N; j += 4) {
+                        const float4 a = *reinterpret_cast<const float4*>(PR + o + j);
+                        const float4 e = *reinterpret_cast<const float4*>(PC + o + j);
+                        yv[j] = uv[j] * (a.x + e.x);
+                        yv[j + 1] = uv[j + 1] * (a.y + e.y);
+                        yv[j + 2] = uv[j + 2] * (a.z + e.z);
+                        yv[j + 3] = uv[j + 3] * (a.w + e.w);
                     }
-                    store_out(gy + base + r * W + col0, yv, nvalid, vec);
+                    if (t_active && r < H) store_out(ys + r * W + col0, yv, N, true);
+                }
+            } else {
+#pragma unroll
+                for (int it = 0; it < kMaxIt; ++it) {
+                    const int r = tr + it * rpi;
+                    if (t_active && r < H) {
+                        float uv[N], yv[N];
+                        unpack(u0[it], uv);
+#pragma unroll
+                        for (int j = 0; j < N; ++j) {
+                            const int o = r * kPitch + col0 + j;
+                            float acc = 0.0f;
+                            if (vec || j < nvalid) {
+                                if (row_any) acc = PR[o];
+                                if (col_any) acc += PC[o];
+                            }
+                            yv[j] = uv[j] * acc;
+                        }
+                        store_out(ys + r * W + col0, yv, nvalid, vec);
+                    }
                 }
             }
+        }
+        if (has_next) {
+            write_xl(x1, l1);
+            load_rows(gu, c + 1, u0);
         }
         __syncthreads();
     }
