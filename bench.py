@@ -38,7 +38,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GSPN scan GB/s and % of HBM peak (4-dir fwd), 1K C-GSPN config"
 HBM_PEAK_GBPS = 8000.0
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_fused_cgspn1k.json")
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fused_scan_kernel_cgspn1k_traffic.txt")
+PROFILE_STATS = os.path.join(ROOT, "profiles", "fused_scan_kernel_cgspn1k_stats.txt")
+COPY_CALIBRATION_BYTES = 256 * 1024 * 1024
 KERNEL_SOURCES = ["linear_spatial_propagation_amd/csrc/gspn_fused.hip",
                   "linear_spatial_propagation_amd/csrc/gspn_device.h"]
 
@@ -63,22 +65,122 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def _read_summary(path):
+    out = {}
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith("#") or ":" not in line:
+                    continue
+                k, v = line.split(":", 1)
+                out[k.strip()] = v.strip()
+    except OSError:
+        pass
+    return out
+
+
 def load_traffic():
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when the kernel source changed since the counters were taken."""
-    try:
-        with open(PROFILE_TRAFFIC) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
+    t = _read_summary(PROFILE_TRAFFIC)
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    try:
+        return int(float(t["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
-def cpu_baseline(cfg_name: str, budget_s: float = 12.0):
-    """Time the fp64 oracle on a bounded sample of the same workload."""
-    import numpy as np
+def _kernel_short(name):
+    if "fused_scan_kernel" in name:
+        return "fused_scan_kernel"
+    if "direction_kernel" in name:
+        return "direction_kernel"
+    if "merge_kernel" in name:
+        return "merge_kernel"
+    if "copyBuffer" in name:
+        return "copy"
+    return name[:48]
+
+
+def summarize_pmc(pmc_dir, command, config="cgspn1k"):
+    """Summarise two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) of a bench
+    run with --copy-calibration into the traffic summary under profiles/.
+
+    FETCH_SIZE / WRITE_SIZE are KiB per dispatch.  Each is scaled by the
+    ratio between the known size of the plain device copy (256 MiB read,
+    256 MiB written) and what the same counter reads for that copy."""
+    import csv
+    import glob
+    from linear_spatial_propagation_amd.inputs import CONFIGS
+    per = {}
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            key = (row["Counter_Name"], int(row["Dispatch_Id"]))
+            per.setdefault(key, [row["Kernel_Name"], 0.0])
+            per[key][1] += float(row["Counter_Value"])
+    vals = {}
+    for (counter, did), (name, v) in per.items():
+        vals.setdefault((counter, _kernel_short(name)), []).append((did, v))
+    copy_w = max(v for _, v in vals[("WRITE_SIZE", "copy")])
+    copy_w_id = [d for d, v in vals[("WRITE_SIZE", "copy")] if v == copy_w][0]
+    copy_f = dict(vals[("FETCH_SIZE", "copy")]).get(copy_w_id)
+    if copy_f is None:   # separate runs number dispatches identically
+        copy_f = max(v for _, v in vals[("FETCH_SIZE", "copy")])
+    copy_kib = COPY_CALIBRATION_BYTES / 1024
+    f_scale, w_scale = copy_kib / copy_f, copy_kib / copy_w
+    fk = [v for _, v in vals[("FETCH_SIZE", "fused_scan_kernel")]]
+    wk = [v for _, v in vals[("WRITE_SIZE", "fused_scan_kernel")]]
+    fetch_kib, write_kib = sum(fk) / len(fk), sum(wk) / len(wk)
+    hbm = fetch_kib * 1024 * f_scale + write_kib * 1024 * w_scale
+    c = CONFIGS[config]
+    alg = algorithmic_bytes(c["B"], c["C"], c["H"], c["W"], 15, c["groups"], c["cpw"], c["dtype"])
+    lines = [
+        f"# rocprofv3 memory counters: fused_scan_kernel<bf16> on {config} "
+        f"(B={c['B']} C={c['C']} H={c['H']} W={c['W']} groups={c['groups']} ch_per_weight={c['cpw']} {c['dtype']})",
+        f"# command (two passes, FETCH_SIZE then WRITE_SIZE): {command}",
+        "# FETCH_SIZE and WRITE_SIZE are KiB per dispatch, averaged over the kernel's dispatches;",
+        "# each is scaled by (known bytes / counter bytes) of a 256 MiB device-to-device copy in the same run.",
+        f"kernel_source_hash: {kernel_source_hash()}",
+        f"dispatches: {len(fk)}",
+        f"fetch_kib_per_dispatch: {fetch_kib:.1f}",
+        f"write_kib_per_dispatch: {write_kib:.1f}",
+        f"copy_known_bytes: {COPY_CALIBRATION_BYTES}",
+        f"copy_fetch_kib: {copy_f:.1f}",
+        f"copy_write_kib: {copy_w:.1f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"hbm_read_bytes_per_launch: {fetch_kib * 1024 * f_scale:.0f}",
+        f"hbm_write_bytes_per_launch: {write_kib * 1024 * w_scale:.0f}",
+        f"hbm_bytes_per_launch: {hbm:.0f}",
+        f"algorithmic_bytes_per_launch: {alg}",
+        f"traffic_over_algorithmic: {hbm / alg:.4f}",
+    ]
+    with open(PROFILE_TRAFFIC, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_stats(stats_csv, command, config="cgspn1k"):
+    """Copy the kernel rows of a rocprofv3 --kernel-trace --stats CSV into the
+    stats summary under profiles/."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 --kernel-trace --stats summary, workload {config}",
+             f"# command: {command}",
+             "kernel, calls, total_ns, average_ns, min_ns, max_ns, percent"]
+    for r in rows:
+        lines.append(f"{_kernel_short(r['Name'])}, {r['Calls']}, {r['TotalDurationNs']}, "
+                     f"{float(r['AverageNs']):.1f}, {r['MinNs']}, {r['MaxNs']}, {float(r['Percentage']):.2f}")
+    lines.append(f"kernel_source_hash: {kernel_source_hash()}")
+    with open(PROFILE_STATS, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cpu_baseline(cfg_name: str, budget_s: float = 8.0):
+    """Time the fp64 oracle on a bounded sample of the same workload: whole
+    batch items, repeated until about budget_s seconds of wall time."""
     import oracle
     from linear_spatial_propagation_amd.inputs import CONFIGS, make_workload
 
@@ -87,20 +189,29 @@ def cpu_baseline(cfg_name: str, budget_s: float = 12.0):
     C, H, W = cfg.pop("C"), cfg.pop("H"), cfg.pop("W")
     threads = oracle.max_threads()
 
-    def run(nb):
+    def prepare(nb):
         wl = make_workload(nb, C, H, W, **cfg)
-        x, w, lam, u = wl.x, wl.w, wl.lam, wl.u
+        return wl, (wl.x, wl.w, wl.lam, wl.u)
+
+    def run(wl, args):
         t0 = time.perf_counter()
-        oracle.scan_fwd(x, w, lam, u, dirs=15, groups=wl.groups, cpw=wl.cpw, nthreads=threads)
+        oracle.scan_fwd(*args, dirs=15, groups=wl.groups, cpw=wl.cpw, nthreads=threads)
         return time.perf_counter() - t0
 
-    t1 = run(1)
-    nb = int(max(1, min(B, budget_s / max(t1, 1e-6))))
-    t = run(nb) if nb > 1 else t1
+    wl, args = prepare(1)
+    t1 = run(wl, args)
+    nb = int(max(1, min(B, budget_s / 4 / max(t1, 1e-6))))
+    if nb > 1:
+        wl, args = prepare(nb)
+    reps, total = 0, 0.0
+    while total < budget_s and reps < 1000:
+        total += run(wl, args)
+        reps += 1
+    t = total / reps
     nbytes = algorithmic_bytes(nb, C, H, W, 15, cfg["groups"], cfg["cpw"], cfg["dtype"])
     return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{nb} of {B} batch items of the same workload ({nb * C} (b,c) slices), "
-                      f"fp64 C oracle, OpenMP over slices, {t:.2f} s"}
+            "sample": f"{nb} of {B} batch items ({nb * C} (b,c) slices) of the same workload, "
+                      f"fp64 C oracle with OpenMP over slices, mean of {reps} runs of {t:.3f} s"}
 
 
 def main():
@@ -111,8 +222,19 @@ def main():
     ap.add_argument("--config", default="cgspn1k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain device copy of known size (for counter calibration)")
+                    help="also run one plain 256 MiB device copy (for counter calibration)")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="write the traffic summary from rocprofv3 --pmc output in DIR and exit")
+    ap.add_argument("--summarize-stats", metavar="CSV",
+                    help="write the kernel-time summary from a rocprofv3 --stats CSV and exit")
+    ap.add_argument("--profile-command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.profile_command, args.config)
+        return
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.profile_command, args.config)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this operator has no cross-GPU step, and runs "
               f"with --gpus {args.gpus} are not part of this build", file=sys.stderr)
@@ -182,7 +304,7 @@ def main():
     hot = np.array([a.elapsed_time(b) for a, b in hot_ev]) * 1e-3
 
     if args.copy_calibration:
-        src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device=dev)
+        src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize(dev)
