@@ -132,6 +132,15 @@ __device__ __forceinline__ void store_out(float* __restrict__ p, const float (&v
 //  and only w0 and w2 occupy registers (64 lines x 2 per lane).
 constexpr int kDepth = 4;
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 __device__ __forceinline__ float line_step(float h, float xl, float w0, float w2) {
     const float dl = from_left(h) - h;
     const float dr = from_right(h) - h;
@@ -285,6 +294,24 @@ __device__ __forceinline__ void scan_any(const ScanCtl& k, const float* X, float
 }
 
 // ---------------------------------------------------------------- staging
+// Raw taps of one (b, k).  Direction dd's [3][H][W] block is found by
+// arithmetic from the global base pointer (no table of pointers), so the
+// compiler keeps the accesses global loads, which only the vector-memory
+// counter tracks (loads through a generic pointer would also hold the LDS
+// counter and serialise every LDS wait behind them).
+__device__ __forceinline__ int first_dir(uint32_t dirs) { return __builtin_ctz(dirs); }
+
+template <typename T>
+struct TapSrc {
+    const T* w;
+    uint32_t dirs;
+    int B, b, Cw, k, HW;
+    __device__ __forceinline__ const T* dir(int dd) const {
+        const int slab = __builtin_popcount(dirs & ((1u << dd) - 1u));
+        return w + ((size_t)(slab * B + b) * Cw + k) * 3 * (size_t)HW;
+    }
+};
+
 // Raw taps of 16 line coordinates [j0, j0+16) of all four directions,
 // loaded as 16-byte vectors (rows that are whole vectors only).  Row
 // directions: thread -> (line jj, vector along the row); column directions:
@@ -298,47 +325,61 @@ struct TapChunk {
     static constexpr int kPasses = 6 / kPairsPerPass;             // (dir pair, tap) = 2 x 3
     uint4 v[2][kPasses];
 
-    __device__ __forceinline__ void load(const T* const (&wsrc)[4], uint32_t dirs, int j0, int H, int W,
+    static constexpr int kLoads = 2 * kPasses;
+
+    // What load i (0 <= i < kLoads) of the chunk at line coordinate j0
+    // fetches: direction group i / kPasses, pass i % kPasses.
+    struct Slot {
+        int dd, t, r, c;
+        bool ok;   // direction enabled and the vector inside the grid
+    };
+    __device__ __forceinline__ static Slot slot(int i, uint32_t dirs, int j0, int H, int W, int tid) {
+        const int grp = i / kPasses, ps = i % kPasses;
+        const int pair = ps * kPairsPerPass + tid / (kChunk * kVPR);   // 0..5
+        Slot q;
+        q.dd = grp * 2 + pair / 3;
+        q.t = pair % 3;
+        const int e = tid % (kChunk * kVPR);
+        if (grp == 0) { q.r = j0 + e / kVPR; q.c = (e % kVPR) * N; }
+        else { q.r = e / (kChunk / N); q.c = j0 + (e % (kChunk / N)) * N; }
+        q.ok = ((dirs >> q.dd) & 1u) && q.r < H && q.c + N <= W;
+        return q;
+    }
+    // The load is unconditional, from an address clamped into the tensor;
+    // store() zeroes what lies outside.  (A load under a divergent branch
+    // makes the compiler's memory-counter waits conservative.)
+    __device__ __forceinline__ void load_one(int i, const TapSrc<T>& wsrc, uint32_t dirs, int j0, int H,
+                                             int W, int HW, int tid) {
+        const Slot q = slot(i, dirs, j0, H, W, tid);
+        const int dd = ((dirs >> q.dd) & 1u) ? q.dd : first_dir(dirs);
+        const T* src = wsrc.dir(dd) + (size_t)q.t * HW + min(q.r, H - 1) * W + min(q.c, W - N);
+        v[i / kPasses][i % kPasses] = *reinterpret_cast<const uint4*>(src);
+    }
+    __device__ __forceinline__ void load(const TapSrc<T>& wsrc, uint32_t dirs, int j0, int H, int W,
                                          int HW, int tid) {
 #pragma unroll
-        for (int grp = 0; grp < 2; ++grp) {
-#pragma unroll
-            for (int ps = 0; ps < kPasses; ++ps) {
-                const int pair = ps * kPairsPerPass + tid / (kChunk * kVPR);   // 0..5
-                const int dd = grp * 2 + pair / 3;
-                const int t = pair % 3;
-                const int e = tid % (kChunk * kVPR);
-                int r, c;
-                if (grp == 0) { r = j0 + e / kVPR; c = (e % kVPR) * N; }
-                else { r = e / (kChunk / N); c = j0 + (e % (kChunk / N)) * N; }
-                const bool ok = ((dirs >> dd) & 1u) && r < H && c + N <= W;
-                v[grp][ps] = ok ? *reinterpret_cast<const uint4*>(wsrc[dd] + (size_t)t * HW + r * W + c)
-                                : make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
+        for (int i = 0; i < kLoads; ++i) load_one(i, wsrc, dirs, j0, H, W, HW, tid);
     }
     // Write as fp32 into S[dir][tap][jj][position] (pitch kPitch).
-    __device__ __forceinline__ void store(float* S, int tid) const {
+    __device__ __forceinline__ void store(float* S, uint32_t dirs, int j0, int H, int W, int tid) const {
 #pragma unroll
-        for (int grp = 0; grp < 2; ++grp) {
+        for (int i = 0; i < kLoads; ++i) {
+            const int grp = i / kPasses, ps = i % kPasses;
+            const Slot q = slot(i, dirs, j0, H, W, tid);
+            uint32_t m = q.ok ? 0xffffffffu : 0u;
+            asm volatile("" : "+v"(m));   // opaque, so the load above stays unconditional
+            const uint4 raw = v[grp][ps];
+            float f[N];
+            unpack(make_uint4(raw.x & m, raw.y & m, raw.z & m, raw.w & m), f);
+            float* Sd = S + (q.dd * 3 + q.t) * kChunk * kPitch;
+            if (grp == 0) {
+                const int jj = q.r - j0;
 #pragma unroll
-            for (int ps = 0; ps < kPasses; ++ps) {
-                const int pair = ps * kPairsPerPass + tid / (kChunk * kVPR);
-                const int dd = grp * 2 + pair / 3;
-                const int t = pair % 3;
-                const int e = tid % (kChunk * kVPR);
-                float f[N];
-                unpack(v[grp][ps], f);
-                float* Sd = S + (dd * 3 + t) * kChunk * kPitch;
-                if (grp == 0) {
-                    const int jj = e / kVPR, c = (e % kVPR) * N;
+                for (int e = 0; e < N; ++e) Sd[jj * kPitch + q.c + e] = f[e];
+            } else {
+                const int jj0 = q.c - j0;
 #pragma unroll
-                    for (int q = 0; q < N; ++q) Sd[jj * kPitch + c + q] = f[q];
-                } else {
-                    const int r = e / (kChunk / N), jj0 = (e % (kChunk / N)) * N;
-#pragma unroll
-                    for (int q = 0; q < N; ++q) Sd[(jj0 + q) * kPitch + r] = f[q];
-                }
+                for (int e = 0; e < N; ++e) Sd[(jj0 + e) * kPitch + q.r] = f[e];
             }
         }
     }
@@ -346,7 +387,7 @@ struct TapChunk {
 
 // Element-wise staging of the same chunk (rows that are not whole vectors).
 template <typename T>
-__device__ __forceinline__ void stage_taps_scalar(float* S, const T* const (&wsrc)[4], uint32_t dirs, int j0,
+__device__ __forceinline__ void stage_taps_scalar(float* S, const TapSrc<T>& wsrc, uint32_t dirs, int j0,
                                                   int H, int W, int HW, int tid) {
     constexpr int kChunk = 16;
     for (int dd = 0; dd < 4; ++dd) {
@@ -358,7 +399,7 @@ __device__ __forceinline__ void stage_taps_scalar(float* S, const T* const (&wsr
                 const int r = j0 + jj;
                 const bool ok = r < H && pp < W;
                 for (int t = 0; t < 3; ++t)
-                    Sd[(t * kChunk + jj) * kPitch + pp] = ok ? to_f32(wsrc[dd][(size_t)t * HW + r * W + pp]) : 0.0f;
+                    Sd[(t * kChunk + jj) * kPitch + pp] = ok ? to_f32(wsrc.dir(dd)[(size_t)t * HW + r * W + pp]) : 0.0f;
             }
         } else {
             const int jj = tid & (kChunk - 1);
@@ -366,14 +407,15 @@ __device__ __forceinline__ void stage_taps_scalar(float* S, const T* const (&wsr
             for (int pp = tid / kChunk; pp < kS; pp += kThreads / kChunk) {
                 const bool ok = q < W && pp < H;
                 for (int t = 0; t < 3; ++t)
-                    Sd[(t * kChunk + jj) * kPitch + pp] = ok ? to_f32(wsrc[dd][(size_t)t * HW + pp * W + q]) : 0.0f;
+                    Sd[(t * kChunk + jj) * kPitch + pp] = ok ? to_f32(wsrc.dir(dd)[(size_t)t * HW + pp * W + q]) : 0.0f;
             }
         }
     }
 }
 
 // ---------------------------------------------------------------- kernel
-template <typename T>
+// VEC: every row is a whole number of 16-byte vectors (W % N == 0).
+template <typename T, bool VEC>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fused_scan_kernel(FusedParams prm) {
     constexpr int N = Vec<T>::N;                     // elements per 16-byte access
@@ -392,7 +434,7 @@ void fused_scan_kernel(FusedParams prm) {
     const int H = prm.H, W = prm.W, B = prm.B, C = prm.C, Cw = prm.Cw;
     const int HW = H * W;
     const uint32_t dirs = prm.dirs;
-    const bool vec = (W % N) == 0;                 // rows are whole 16-byte vectors
+    constexpr bool vec = VEC;
 
     // ---- which (b, k, chunk) this workgroup owns
     const int wg = blockIdx.x;
@@ -432,7 +474,12 @@ void fused_scan_kernel(FusedParams prm) {
 #pragma unroll
         for (int it = 0; it < kMaxIt; ++it) {
             const int r = tr + it * rpi;
-            if (t_active && r < H) dst[it] = load_raw(sl + r * W + col0, nvalid, vec);
+            if constexpr (VEC) {
+                // unconditional, row clamped (see TapChunk::load_one)
+                dst[it] = *reinterpret_cast<const uint4*>(sl + min(r, H - 1) * W + col0);
+            } else {
+                if (t_active && r < H) dst[it] = load_raw(sl + r * W + col0, nvalid, vec);
+            }
         }
     };
     // XL <- lambda * x (fp32, pitch kPitch)
@@ -462,47 +509,72 @@ void fused_scan_kernel(FusedParams prm) {
     // x / lambda of the next channel and u of the current one travel in
     // registers; the first channel's loads are in flight during the prologue
     uint4 x1[kMaxIt], l1[kMaxIt], u0[kMaxIt];
-    load_rows(gx, c_begin, x1);
-    load_rows(glam, c_begin, l1);
-    load_rows(gu, c_begin, u0);
 
     // ---- prologue: normalised taps of this direction, indexed by line
     // coordinate j (row for TB/BT, column for LR/RL).  The taps of 16 line
     // coordinates of every direction are staged in LDS as fp32 [dir][tap]
     // [j][position] (pitch kPitch), transposed for LR/RL; every wave then
-    // reads its taps along its lanes.  The next chunk's loads are in flight
-    // while the current chunk is normalised.  Entries outside the grid are
-    // staged as 0, which keeps idle lanes finite.
+    // reads its taps along its lanes.  Entries outside the grid are staged
+    // as 0, which keeps idle lanes finite.
+    //
+    // Load schedule (whole-vector rows): chunk 0 is loaded up front; the
+    // loads of chunks 1.. and then of the first channel's x / lambda / u
+    // rows are issued one at a time between normalised lines, kSlots per
+    // chunk, so that the memory pipe stays busy while the VALU normalises
+    // and no wave stalls on a long burst of loads.
     float w0[kS], w2[kS];
     {
         float* S = lds;   // [4][3][kChunk][kPitch]
-        const T* wsrc[4];
-        for (int dd = 0; dd < 4; ++dd) {
-            const int slab = __builtin_popcount(dirs & ((1u << dd) - 1u));
-            wsrc[dd] = gw + ((size_t)(slab * B + b) * Cw + k) * 3 * (size_t)HW;
+        const TapSrc<T> wsrc{gw, dirs, B, b, Cw, k, HW};
+        constexpr int kNCh = kS / kChunk;
+        constexpr int kLd = TapChunk<T>::kLoads;
+        constexpr int kTapItems = (kNCh - 1) * kLd;     // items [0, kTapItems): tap loads of chunks 1..
+        constexpr int kItems = kTapItems + 3 * kMaxIt;  // then x, lambda, u rows
+        constexpr int kSlots = (kItems + kNCh - 1) / kNCh > 8 ? (kItems + kNCh - 1) / kNCh : 8;
+        constexpr int kSlotStep = kSlots <= kChunk / 2 ? 2 : 1;   // odd lines when they fit
+        static_assert(kSlots <= kChunk && kItems <= kSlots * kNCh, "issue slots");
+        static_assert(kSlots >= kLd, "chunk c + 1 is issued while chunk c is normalised");
+        TapChunk<T> tapv[kNCh];
+        if constexpr (VEC) {
+            tapv[0].load(wsrc, dirs, 0, H, W, HW, tid);
+        } else {
+            load_rows(gx, c_begin, x1);
+            load_rows(glam, c_begin, l1);
+            load_rows(gu, c_begin, u0);
         }
-        TapChunk<T> tapv;
-        if (vec) tapv.load(wsrc, dirs, 0, H, W, HW, tid);
-#pragma unroll
-        for (int ch = 0; ch < kS / kChunk; ++ch) {
-            const int j0 = ch * kChunk;
-            if (vec) {
-                tapv.store(S, tid);
-                if (ch + 1 < kS / kChunk) tapv.load(wsrc, dirs, j0 + kChunk, H, W, HW, tid);
-            } else {
-                stage_taps_scalar<T>(S, wsrc, dirs, j0, H, W, HW, tid);
-            }
+        static_for<0, kNCh>([&](auto chc) {
+            constexpr int ch = decltype(chc)::value;
+            constexpr int j0 = ch * kChunk;
+            if constexpr (VEC) tapv[ch].store(S, dirs, j0, H, W, tid);
+            else stage_taps_scalar<T>(S, wsrc, dirs, j0, H, W, HW, tid);
             __syncthreads();
             const float* Sw = S + d * 3 * kChunk * kPitch + p;
-#pragma unroll
-            for (int jj = 0; jj < kChunk; ++jj) {
+            static_for<0, kChunk>([&](auto jjc) {
+                constexpr int jj = decltype(jjc)::value;
+                constexpr int g = kSlots * ch + jj / kSlotStep;   // item issued before this line
+                if constexpr (VEC && jj % kSlotStep == kSlotStep - 1 && jj / kSlotStep < kSlots && g < kItems) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (g < kTapItems) {
+                        constexpr int cn = 1 + g / kLd;
+                        tapv[cn].load_one(g % kLd, wsrc, dirs, cn * kChunk, H, W, HW, tid);
+                    } else {
+                        constexpr int q = g - kTapItems;
+                        constexpr int it = q % kMaxIt;
+                        const int r = min(tr + it * rpi, H - 1);
+                        const size_t o = ((size_t)b * C + c_begin) * (size_t)HW + r * W + col0;
+                        if constexpr (q / kMaxIt == 0) x1[it] = *reinterpret_cast<const uint4*>(gx + o);
+                        else if constexpr (q / kMaxIt == 1) l1[it] = *reinterpret_cast<const uint4*>(glam + o);
+                        else u0[it] = *reinterpret_cast<const uint4*>(gu + o);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 const Taps tp = normalise_taps(Sw[jj * kPitch], Sw[(kChunk + jj) * kPitch],
                                                Sw[(2 * kChunk + jj) * kPitch], has0, has2);
                 w0[j0 + jj] = tp.w0;
                 w2[j0 + jj] = tp.w2;
-            }
+            });
             __syncthreads();
-        }
+        });
     }
 
     // padding rows/columns of XL must read as zero
@@ -527,11 +599,14 @@ void fused_scan_kernel(FusedParams prm) {
     ctl.cnt2 = n - nstore;
 
     for (int c = c_begin; c < c_end; ++c) {
-        const bool has_next = c + 1 < c_end;
-        if (has_next) {
-            load_rows(gx, c + 1, x1);
-            load_rows(glam, c + 1, l1);
-        }
+        // Next channel's x / lambda (and below u) are loaded without a
+        // condition: the last channel reloads itself (a cache hit) and the
+        // XL it writes is never read.  Loads and their use under separate
+        // conditions would make the compiler's counter waits at the loop
+        // head conservative (waiting for u in flight).
+        const int cn = min(c + 1, c_end - 1);
+        load_rows(gx, cn, x1);
+        load_rows(glam, cn, l1);
 
         // ---- scan: the first part stores, the second adds onto the partner
         float h = 0.0f;
@@ -586,10 +661,8 @@ void fused_scan_kernel(FusedParams prm) {
                 }
             }
         }
-        if (has_next) {
-            write_xl(x1, l1);
-            load_rows(gu, c + 1, u0);
-        }
+        write_xl(x1, l1);
+        load_rows(gu, cn, u0);
         __syncthreads();
     }
 }
@@ -610,10 +683,14 @@ hipError_t launch_fused(const ScanArgs& a, hipStream_t stream) {
     p.chunk_len = (a.cpw + nchunk - 1) / nchunk;
     p.nchunk = (a.cpw + p.chunk_len - 1) / p.chunk_len;
     const unsigned grid = (unsigned)(sets * p.nchunk);
-    if (a.bf16)
-        hipLaunchKernelGGL(fused_scan_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(fused_scan_kernel<float>, dim3(grid), dim3(kThreads), 0, stream, p);
+    const bool vec = a.W % (a.bf16 ? Vec<uint16_t>::N : Vec<float>::N) == 0;
+    if (a.bf16) {
+        if (vec) hipLaunchKernelGGL((fused_scan_kernel<uint16_t, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL((fused_scan_kernel<uint16_t, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    } else {
+        if (vec) hipLaunchKernelGGL((fused_scan_kernel<float, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL((fused_scan_kernel<float, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
