@@ -99,11 +99,15 @@ __device__ __forceinline__ void unpack(uint4 r, float (&o)[4]) {
     o[2] = __uint_as_float(r.z); o[3] = __uint_as_float(r.w);
 }
 
+// y is written once and not read again by the kernel: stores are
+// non-temporal (streamed out of the L2 instead of left dirty in it, which
+// the end of the kernel would otherwise have to write back).
 __device__ __forceinline__ void store_out(uint16_t* __restrict__ p, const float (&v)[8], int nvalid, bool vec) {
     if (vec) {
-        uint4 r = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                             pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-        *reinterpret_cast<uint4*>(p) = r;
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 r = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                   pack_bf16x2(v[6], v[7])};
+        __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p));
     } else {
         for (int j = 0; j < 8; ++j)
             if (j < nvalid) p[j] = from_f32(v[j], (uint16_t*)nullptr);
@@ -111,11 +115,19 @@ __device__ __forceinline__ void store_out(uint16_t* __restrict__ p, const float 
 }
 __device__ __forceinline__ void store_out(float* __restrict__ p, const float (&v)[4], int nvalid, bool vec) {
     if (vec) {
-        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 r = {v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(p));
     } else {
         for (int j = 0; j < 4; ++j)
             if (j < nvalid) p[j] = v[j];
     }
+}
+
+// 16-byte load (x, lambda, u, taps; 16-byte aligned).
+template <typename T>
+__device__ __forceinline__ uint4 load16(const T* p) {
+    return *reinterpret_cast<const uint4*>(p);
 }
 
 // ---------------------------------------------------------------- scan
@@ -353,7 +365,7 @@ struct TapChunk {
         const Slot q = slot(i, dirs, j0, H, W, tid);
         const int dd = ((dirs >> q.dd) & 1u) ? q.dd : first_dir(dirs);
         const T* src = wsrc.dir(dd) + (size_t)q.t * HW + min(q.r, H - 1) * W + min(q.c, W - N);
-        v[i / kPasses][i % kPasses] = *reinterpret_cast<const uint4*>(src);
+        v[i / kPasses][i % kPasses] = load16(src);
     }
     __device__ __forceinline__ void load(const TapSrc<T>& wsrc, uint32_t dirs, int j0, int H, int W,
                                          int HW, int tid) {
@@ -476,7 +488,7 @@ void fused_scan_kernel(FusedParams prm) {
             const int r = tr + it * rpi;
             if constexpr (VEC) {
                 // unconditional, row clamped (see TapChunk::load_one)
-                dst[it] = *reinterpret_cast<const uint4*>(sl + min(r, H - 1) * W + col0);
+                dst[it] = load16(sl + min(r, H - 1) * W + col0);
             } else {
                 if (t_active && r < H) dst[it] = load_raw(sl + r * W + col0, nvalid, vec);
             }
@@ -562,9 +574,9 @@ void fused_scan_kernel(FusedParams prm) {
                         constexpr int it = q % kMaxIt;
                         const int r = min(tr + it * rpi, H - 1);
                         const size_t o = ((size_t)b * C + c_begin) * (size_t)HW + r * W + col0;
-                        if constexpr (q / kMaxIt == 0) x1[it] = *reinterpret_cast<const uint4*>(gx + o);
-                        else if constexpr (q / kMaxIt == 1) l1[it] = *reinterpret_cast<const uint4*>(glam + o);
-                        else u0[it] = *reinterpret_cast<const uint4*>(gu + o);
+                        if constexpr (q / kMaxIt == 0) x1[it] = load16(gx + o);
+                        else if constexpr (q / kMaxIt == 1) l1[it] = load16(glam + o);
+                        else u0[it] = load16(gu + o);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }

@@ -104,7 +104,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(GeneralParams prm, size
     for (size_t e = (size_t)blockIdx.x * kThreads + threadIdx.x; e < E; e += (size_t)gridDim.x * kThreads) {
         float acc = 0.0f;
         for (int s = 0; s < prm.nd; ++s) acc += prm.planes[(size_t)s * E + e];
-        gy[e] = from_f32(to_f32(gu[e]) * acc, (T*)nullptr);
+        // y is not read again: non-temporal store
+        __builtin_nontemporal_store(from_f32(to_f32(gu[e]) * acc, (T*)nullptr), gy + e);
     }
 }
 
