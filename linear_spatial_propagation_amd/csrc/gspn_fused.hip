@@ -269,7 +269,7 @@ __device__ __forceinline__ void scan_general(const float* __restrict__ X, float*
 struct ScanCtl {
     int d;          // direction 0..3 (TB, BT, LR, RL)
     int p;          // lane = position on the line
-    bool fast;      // global scan of kS lines with both directions of the pair on
+    bool fast;      // global scan (one group) with both directions of the pair on
     int L;          // lines per group
     int skip1, cnt1, skip2, cnt2;  // general form: store part, add part
 };
@@ -468,7 +468,9 @@ void fused_scan_kernel(FusedParams prm) {
     const int n = is_row ? H : W;      // lines
     const int m = is_row ? W : H;      // positions per line
     const int L = n / prm.groups;      // lines per group
-    const bool has0 = p >= 1;
+    // Taps toward p-1 / p+1 exist.  Lanes past the line (p >= m) get
+    // neither, so their weights are w0 = w2 = 0 and their state stays 0.
+    const bool has0 = p >= 1 && p < m;
     const bool has2 = p + 1 < m;
 
     // ---- x / lambda / u rows: N elements per thread
@@ -535,6 +537,7 @@ void fused_scan_kernel(FusedParams prm) {
     // chunk, so that the memory pipe stays busy while the VALU normalises
     // and no wave stalls on a long burst of loads.
     float w0[kS], w2[kS];
+    const int first_line = asc ? 0 : n - 1;
     {
         float* S = lds;   // [4][3][kChunk][kPitch]
         const TapSrc<T> wsrc{gw, dirs, B, b, Cw, k, HW};
@@ -582,8 +585,12 @@ void fused_scan_kernel(FusedParams prm) {
                 }
                 const Taps tp = normalise_taps(Sw[jj * kPitch], Sw[(kChunk + jj) * kPitch],
                                                Sw[(2 * kChunk + jj) * kPitch], has0, has2);
-                w0[j0 + jj] = tp.w0;
-                w2[j0 + jj] = tp.w2;
+                // the first line of the scan never uses its taps (they may
+                // hold anything); the static form still multiplies its
+                // weights by zero differences, so they must be finite
+                const bool first = j0 + jj == first_line;
+                w0[j0 + jj] = first ? 0.0f : tp.w0;
+                w2[j0 + jj] = first ? 0.0f : tp.w2;
             });
             __syncthreads();
         });
@@ -603,7 +610,11 @@ void fused_scan_kernel(FusedParams prm) {
     ScanCtl ctl;
     ctl.d = d;
     ctl.p = p;
-    ctl.fast = n == kS && L == kS && partner_on;
+    // The static form runs all kS lines of the padded 64 x 64 planes.  With
+    // fewer lines or positions it is still exact: padded XL is zero, padded
+    // lanes keep h = 0 (w0 = w2 = 0), and a descending scan meets its first
+    // real line with h = 0, so that line gets h = lambda x, the restart.
+    ctl.fast = L == n && partner_on;
     ctl.L = L;
     ctl.skip1 = asc ? 0 : kS - n;          // general form: first visited
     ctl.cnt1 = nstore;                     // line coordinate is 0 (asc)
