@@ -108,4 +108,19 @@ __device__ __forceinline__ Taps normalise_taps(float a0, float a1, float a2, boo
     return r;
 }
 
+// normalise_taps' fast form alone, for staged taps that are already
+// sanitised: finite, >= -40, and 0 where a tap is missing or unused (any
+// finite value gives the same weights there, since the missing tap's
+// product term is dropped and its q cancels).  Returns (w0, w2).
+__device__ __forceinline__ float2 normalise_fast(float a0, float a1, float a2, bool has0, bool has2) {
+    const float kNegLog2e = -1.44269504088896340736f;
+    const float q0 = 1.0f + fast_exp2(a0 * kNegLog2e);
+    const float q1 = 1.0f + fast_exp2(a1 * kNegLog2e);
+    const float q2 = 1.0f + fast_exp2(a2 * kNegLog2e);
+    const float p12 = has0 ? q1 * q2 : 0.0f;
+    const float p01 = has2 ? q0 * q1 : 0.0f;
+    const float inv = fast_rcp(fmaf(q0, q2, p12) + p01);
+    return make_float2(p12 * inv, p01 * inv);
+}
+
 }  // namespace gspn

@@ -324,103 +324,112 @@ struct TapSrc {
     }
 };
 
-// Raw taps of 16 line coordinates [j0, j0+16) of all four directions,
-// loaded as 16-byte vectors (rows that are whole vectors only).  Row
-// directions: thread -> (line jj, vector along the row); column directions:
-// thread -> (row r, vector along the 16 columns).
+// Raw taps of 16 line coordinates [j0, j0+16) of the calling wave's own
+// direction d, loaded as 16-byte vectors (rows that are whole vectors
+// only) and staged in the wave's own LDS region S[d][tap][jj][position]
+// (fp32, pitch kPitch).  Since every wave stages and reads only its own
+// direction, the prologue needs no workgroup barrier between chunks.
+//   Row directions: lane -> (line jj, vector along the row), 8 lanes per
+//   128-byte row.  Column directions: lane -> (row r, vector along the 16
+//   columns), written transposed.
 template <typename T>
 struct TapChunk {
     static constexpr int N = Vec<T>::N;
     static constexpr int kChunk = 16;
-    static constexpr int kVPR = kS / N;                           // vectors per 64-wide row
-    static constexpr int kPairsPerPass = kThreads / (kChunk * kVPR);
-    static constexpr int kPasses = 6 / kPairsPerPass;             // (dir pair, tap) = 2 x 3
-    uint4 v[2][kPasses];
+    static constexpr int kVPR = kS / N;                 // vectors per 64-wide row
+    static constexpr int kPerTap = kChunk * kVPR;       // vectors per tap and chunk
+    static constexpr int kLoads = 3 * kPerTap / 64;     // per lane
+    uint4 v[kLoads];
 
-    static constexpr int kLoads = 2 * kPasses;
-
-    // What load i (0 <= i < kLoads) of the chunk at line coordinate j0
-    // fetches: direction group i / kPasses, pass i % kPasses.
     struct Slot {
-        int dd, t, r, c;
+        int t, r, c;
         bool ok;   // direction enabled and the vector inside the grid
     };
-    __device__ __forceinline__ static Slot slot(int i, uint32_t dirs, int j0, int H, int W, int tid) {
-        const int grp = i / kPasses, ps = i % kPasses;
-        const int pair = ps * kPairsPerPass + tid / (kChunk * kVPR);   // 0..5
+    __device__ __forceinline__ static Slot slot(int i, int d, uint32_t dirs, int j0, int H, int W, int lane) {
+        const int u = lane + 64 * i;
         Slot q;
-        q.dd = grp * 2 + pair / 3;
-        q.t = pair % 3;
-        const int e = tid % (kChunk * kVPR);
-        if (grp == 0) { q.r = j0 + e / kVPR; q.c = (e % kVPR) * N; }
+        q.t = u / kPerTap;
+        const int e = u % kPerTap;
+        if (d < 2) { q.r = j0 + e / kVPR; q.c = (e % kVPR) * N; }
         else { q.r = e / (kChunk / N); q.c = j0 + (e % (kChunk / N)) * N; }
-        q.ok = ((dirs >> q.dd) & 1u) && q.r < H && q.c + N <= W;
+        q.ok = ((dirs >> d) & 1u) && q.r < H && q.c + N <= W;
         return q;
+    }
+    // Staged values are sanitised for normalise_fast: besides everything
+    // outside the grid, the taps that are never used -- a missing tap (tap
+    // 0 at position 0, tap 2 at position m-1) and all taps of the scan's
+    // first line -- are staged as 0.  Row directions: line = row, position
+    // = column; column directions: the other way round.
+    __device__ __forceinline__ static bool vector_used(const Slot& q, int d, int first_line, int H) {
+        if (d < 2) return q.r != first_line;
+        return !((q.t == 0 && q.r == 0) || (q.t == 2 && q.r == H - 1));
     }
     // The load is unconditional, from an address clamped into the tensor;
     // store() zeroes what lies outside.  (A load under a divergent branch
     // makes the compiler's memory-counter waits conservative.)
-    __device__ __forceinline__ void load_one(int i, const TapSrc<T>& wsrc, uint32_t dirs, int j0, int H,
-                                             int W, int HW, int tid) {
-        const Slot q = slot(i, dirs, j0, H, W, tid);
-        const int dd = ((dirs >> q.dd) & 1u) ? q.dd : first_dir(dirs);
+    __device__ __forceinline__ void load_one(int i, const TapSrc<T>& wsrc, int d, uint32_t dirs, int j0, int H,
+                                             int W, int HW, int lane) {
+        const Slot q = slot(i, d, dirs, j0, H, W, lane);
+        const int dd = ((dirs >> d) & 1u) ? d : first_dir(dirs);
         const T* src = wsrc.dir(dd) + (size_t)q.t * HW + min(q.r, H - 1) * W + min(q.c, W - N);
-        v[i / kPasses][i % kPasses] = load16(src);
+        v[i] = load16(src);
     }
-    __device__ __forceinline__ void load(const TapSrc<T>& wsrc, uint32_t dirs, int j0, int H, int W,
-                                         int HW, int tid) {
+    __device__ __forceinline__ void load(const TapSrc<T>& wsrc, int d, uint32_t dirs, int j0, int H, int W,
+                                         int HW, int lane) {
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) load_one(i, wsrc, dirs, j0, H, W, HW, tid);
+        for (int i = 0; i < kLoads; ++i) load_one(i, wsrc, d, dirs, j0, H, W, HW, lane);
     }
-    // Write as fp32 into S[dir][tap][jj][position] (pitch kPitch).
-    __device__ __forceinline__ void store(float* S, uint32_t dirs, int j0, int H, int W, int tid) const {
+    // Write as fp32 into the wave's region Sd = S[d] ([tap][jj][position]).
+    __device__ __forceinline__ void store(float* Sd, int d, uint32_t dirs, int j0, int H, int W, int first_line,
+                                          int lane) const {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
-            const int grp = i / kPasses, ps = i % kPasses;
-            const Slot q = slot(i, dirs, j0, H, W, tid);
-            uint32_t m = q.ok ? 0xffffffffu : 0u;
+            const Slot q = slot(i, d, dirs, j0, H, W, lane);
+            uint32_t m = q.ok && vector_used(q, d, first_line, H) ? 0xffffffffu : 0u;
             asm volatile("" : "+v"(m));   // opaque, so the load above stays unconditional
-            const uint4 raw = v[grp][ps];
             float f[N];
-            unpack(make_uint4(raw.x & m, raw.y & m, raw.z & m, raw.w & m), f);
-            float* Sd = S + (q.dd * 3 + q.t) * kChunk * kPitch;
-            if (grp == 0) {
+            unpack(make_uint4(v[i].x & m, v[i].y & m, v[i].z & m, v[i].w & m), f);
+            // unused elements at the vector's ends
+            if (d < 2) {
+                if (q.t == 0 && q.c == 0) f[0] = 0.0f;               // position 0 has no tap 0
+                if (q.t == 2 && q.c + N == W) f[N - 1] = 0.0f;       // position W-1 has no tap 2
+            } else {
+                if (q.c == first_line) f[0] = 0.0f;                  // first line (column)
+                if (q.c + N - 1 == first_line) f[N - 1] = 0.0f;
+            }
+            float* St = Sd + q.t * kChunk * kPitch;
+            if (d < 2) {
                 const int jj = q.r - j0;
 #pragma unroll
-                for (int e = 0; e < N; ++e) Sd[jj * kPitch + q.c + e] = f[e];
+                for (int e = 0; e < N; ++e) St[jj * kPitch + q.c + e] = f[e];
             } else {
                 const int jj0 = q.c - j0;
 #pragma unroll
-                for (int e = 0; e < N; ++e) Sd[(jj0 + e) * kPitch + q.r] = f[e];
+                for (int e = 0; e < N; ++e) St[(jj0 + e) * kPitch + q.r] = f[e];
             }
         }
     }
 };
 
-// Element-wise staging of the same chunk (rows that are not whole vectors).
+// Element-wise staging of the same chunk into the wave's own region (rows
+// that are not whole vectors).
 template <typename T>
-__device__ __forceinline__ void stage_taps_scalar(float* S, const TapSrc<T>& wsrc, uint32_t dirs, int j0,
-                                                  int H, int W, int HW, int tid) {
+__device__ __forceinline__ void stage_taps_scalar(float* Sd, const TapSrc<T>& wsrc, int d, uint32_t dirs, int j0,
+                                                  int H, int W, int HW, int first_line, int lane) {
     constexpr int kChunk = 16;
-    for (int dd = 0; dd < 4; ++dd) {
-        if (!((dirs >> dd) & 1u)) continue;
-        float* Sd = S + dd * 3 * kChunk * kPitch;
-        if (dd < 2) {
-            const int pp = tid & 63;
-            for (int jj = tid >> 6; jj < kChunk; jj += kThreads / 64) {
-                const int r = j0 + jj;
-                const bool ok = r < H && pp < W;
-                for (int t = 0; t < 3; ++t)
-                    Sd[(t * kChunk + jj) * kPitch + pp] = ok ? to_f32(wsrc.dir(dd)[(size_t)t * HW + r * W + pp]) : 0.0f;
-            }
-        } else {
-            const int jj = tid & (kChunk - 1);
-            const int q = j0 + jj;
-            for (int pp = tid / kChunk; pp < kS; pp += kThreads / kChunk) {
-                const bool ok = q < W && pp < H;
-                for (int t = 0; t < 3; ++t)
-                    Sd[(t * kChunk + jj) * kPitch + pp] = ok ? to_f32(wsrc.dir(dd)[(size_t)t * HW + pp * W + q]) : 0.0f;
-            }
+    if (!((dirs >> d) & 1u)) return;
+    const T* src = wsrc.dir(d);
+    for (int jj = 0; jj < kChunk; ++jj) {
+        // row directions: line = row j0+jj, lane = column; column
+        // directions: line = column j0+jj, lane = row
+        const int r = d < 2 ? j0 + jj : lane;
+        const int q = d < 2 ? lane : j0 + jj;
+        const int line = d < 2 ? r : q, pos = d < 2 ? q : r, m = d < 2 ? W : H;
+        const bool ok = r < H && q < W && line != first_line;
+        for (int t = 0; t < 3; ++t) {
+            // unused taps are staged as 0 (see TapChunk::vector_used)
+            const bool used = ok && !(t == 0 && pos == 0) && !(t == 2 && pos == m - 1);
+            Sd[(t * kChunk + jj) * kPitch + lane] = used ? to_f32(src[(size_t)t * HW + r * W + q]) : 0.0f;
         }
     }
 }
@@ -525,11 +534,12 @@ void fused_scan_kernel(FusedParams prm) {
     uint4 x1[kMaxIt], l1[kMaxIt], u0[kMaxIt];
 
     // ---- prologue: normalised taps of this direction, indexed by line
-    // coordinate j (row for TB/BT, column for LR/RL).  The taps of 16 line
-    // coordinates of every direction are staged in LDS as fp32 [dir][tap]
-    // [j][position] (pitch kPitch), transposed for LR/RL; every wave then
-    // reads its taps along its lanes.  Entries outside the grid are staged
-    // as 0, which keeps idle lanes finite.
+    // coordinate j (row for TB/BT, column for LR/RL).  Each wave stages the
+    // taps of 16 line coordinates of its own direction in its own LDS
+    // region as fp32 [tap][j][position] (pitch kPitch), transposed for
+    // LR/RL, and reads them along its lanes: no workgroup barrier is needed
+    // between chunks, so waves do not wait on each other's loads.  Entries
+    // outside the grid are staged as 0, which keeps idle lanes finite.
     //
     // Load schedule (whole-vector rows): chunk 0 is loaded up front; the
     // loads of chunks 1.. and then of the first channel's x / lambda / u
@@ -543,15 +553,23 @@ void fused_scan_kernel(FusedParams prm) {
         const TapSrc<T> wsrc{gw, dirs, B, b, Cw, k, HW};
         constexpr int kNCh = kS / kChunk;
         constexpr int kLd = TapChunk<T>::kLoads;
-        constexpr int kTapItems = (kNCh - 1) * kLd;     // items [0, kTapItems): tap loads of chunks 1..
-        constexpr int kItems = kTapItems + 3 * kMaxIt;  // then x, lambda, u rows
-        constexpr int kSlots = (kItems + kNCh - 1) / kNCh > 8 ? (kItems + kNCh - 1) / kNCh : 8;
+#ifndef GSPN_TAP_AHEAD
+#define GSPN_TAP_AHEAD 2
+#endif
+#ifndef GSPN_SLOTS
+#define GSPN_SLOTS 8
+#endif
+        constexpr int kAhead = GSPN_TAP_AHEAD;               // chunks loaded up front
+        constexpr int kTapItems = (kNCh - kAhead) * kLd;     // items [0, kTapItems): tap loads of chunks kAhead..
+        constexpr int kItems = kTapItems + 3 * kMaxIt;       // then x, lambda, u rows
+        constexpr int kSlots = (kItems + kNCh - 1) / kNCh > GSPN_SLOTS ? (kItems + kNCh - 1) / kNCh : GSPN_SLOTS;
         constexpr int kSlotStep = kSlots <= kChunk / 2 ? 2 : 1;   // odd lines when they fit
         static_assert(kSlots <= kChunk && kItems <= kSlots * kNCh, "issue slots");
-        static_assert(kSlots >= kLd, "chunk c + 1 is issued while chunk c is normalised");
+        static_assert(kAhead > 1 || kSlots >= kLd, "chunk c + 1 is issued while chunk c is normalised");
         TapChunk<T> tapv[kNCh];
         if constexpr (VEC) {
-            tapv[0].load(wsrc, dirs, 0, H, W, HW, tid);
+#pragma unroll
+            for (int ch = 0; ch < kAhead; ++ch) tapv[ch].load(wsrc, d, dirs, ch * kChunk, H, W, HW, p);
         } else {
             load_rows(gx, c_begin, x1);
             load_rows(glam, c_begin, l1);
@@ -560,18 +578,19 @@ void fused_scan_kernel(FusedParams prm) {
         static_for<0, kNCh>([&](auto chc) {
             constexpr int ch = decltype(chc)::value;
             constexpr int j0 = ch * kChunk;
-            if constexpr (VEC) tapv[ch].store(S, dirs, j0, H, W, tid);
-            else stage_taps_scalar<T>(S, wsrc, dirs, j0, H, W, HW, tid);
-            __syncthreads();
-            const float* Sw = S + d * 3 * kChunk * kPitch + p;
+            float* const Sd = S + d * 3 * kChunk * kPitch;   // this wave's region
+            if constexpr (VEC) tapv[ch].store(Sd, d, dirs, j0, H, W, first_line, p);
+            else stage_taps_scalar<T>(Sd, wsrc, d, dirs, j0, H, W, HW, first_line, p);
+            const float* Sw = Sd + p;
+            float amin = 0.0f;   // smallest staged tap of this chunk (staged unused taps are 0)
             static_for<0, kChunk>([&](auto jjc) {
                 constexpr int jj = decltype(jjc)::value;
                 constexpr int g = kSlots * ch + jj / kSlotStep;   // item issued before this line
                 if constexpr (VEC && jj % kSlotStep == kSlotStep - 1 && jj / kSlotStep < kSlots && g < kItems) {
                     __builtin_amdgcn_sched_barrier(0);
                     if constexpr (g < kTapItems) {
-                        constexpr int cn = 1 + g / kLd;
-                        tapv[cn].load_one(g % kLd, wsrc, dirs, cn * kChunk, H, W, HW, tid);
+                        constexpr int cn = kAhead + g / kLd;
+                        tapv[cn].load_one(g % kLd, wsrc, d, dirs, cn * kChunk, H, W, HW, p);
                     } else {
                         constexpr int q = g - kTapItems;
                         constexpr int it = q % kMaxIt;
@@ -583,17 +602,25 @@ void fused_scan_kernel(FusedParams prm) {
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                const Taps tp = normalise_taps(Sw[jj * kPitch], Sw[(kChunk + jj) * kPitch],
-                                               Sw[(2 * kChunk + jj) * kPitch], has0, has2);
-                // the first line of the scan never uses its taps (they may
-                // hold anything); the static form still multiplies its
-                // weights by zero differences, so they must be finite
-                const bool first = j0 + jj == first_line;
-                w0[j0 + jj] = first ? 0.0f : tp.w0;
-                w2[j0 + jj] = first ? 0.0f : tp.w2;
+                const float a0 = Sw[jj * kPitch], a1 = Sw[(kChunk + jj) * kPitch], a2 = Sw[(2 * kChunk + jj) * kPitch];
+                amin = fminf(amin, fminf(fminf(a0, a1), a2));
+                const float2 w = normalise_fast(a0, a1, a2, has0, has2);
+                w0[j0 + jj] = w.x;
+                w2[j0 + jj] = w.y;
             });
-            __syncthreads();
+            // a tap below -40 anywhere in the wave's chunk: redo the chunk
+            // with the exact-form branches (rare: N(0,1) taps never get there)
+            if (__builtin_amdgcn_ballot_w64(amin < -40.0f) != 0) {
+                static_for<0, kChunk>([&](auto jjc) {
+                    constexpr int jj = decltype(jjc)::value;
+                    const Taps tp = normalise_taps(Sw[jj * kPitch], Sw[(kChunk + jj) * kPitch],
+                                                   Sw[(2 * kChunk + jj) * kPitch], has0, has2);
+                    w0[j0 + jj] = tp.w0;
+                    w2[j0 + jj] = tp.w2;
+                });
+            }
         });
+        __syncthreads();   // every wave is done with the staging area (it becomes XL)
     }
 
     // padding rows/columns of XL must read as zero
