@@ -110,13 +110,15 @@ int gspn_scan_fwd_path(const void* x, const void* w_raw, const void* lam, const 
         if (e != hipSuccess) { set_error("fused kernel launch", e); return GSPN_ERR_HIP; }
         return GSPN_OK;
     }
-    // general path: stream-ordered fp32 workspace, one plane per direction
-    float* planes = nullptr;
-    const size_t pbytes = (size_t)popcount4(dirs) * E * sizeof(float);
-    hipError_t e = hipMallocAsync((void**)&planes, pbytes, stream);
+    // general path: stream-ordered workspace (line kernels when the sides
+    // allow, else the per-line fallback)
+    const bool lines = gspn::lines_supported(a.H, a.W);
+    const size_t pbytes = lines ? gspn::lines_workspace_bytes(a) : (size_t)popcount4(dirs) * E * sizeof(float);
+    void* work = nullptr;
+    hipError_t e = hipMallocAsync(&work, pbytes, stream);
     if (e != hipSuccess) { set_error("hipMallocAsync(workspace)", e); return GSPN_ERR_HIP; }
-    e = gspn::launch_general(a, planes, stream);
-    const hipError_t ef = hipFreeAsync(planes, stream);
+    e = lines ? gspn::launch_lines(a, work, stream) : gspn::launch_general(a, static_cast<float*>(work), stream);
+    const hipError_t ef = hipFreeAsync(work, stream);
     if (e != hipSuccess) { set_error("general kernel launch", e); return GSPN_ERR_HIP; }
     if (ef != hipSuccess) { set_error("hipFreeAsync(workspace)", ef); return GSPN_ERR_HIP; }
     return GSPN_OK;

@@ -24,7 +24,26 @@ struct ScanArgs {
 constexpr int kFusedMaxSide = 64;
 hipError_t launch_fused(const ScanArgs& a, hipStream_t stream);
 
-// General path: any H, W <= 4096.  `planes` is an fp32 workspace of
+// Line path: H, W <= kLinesMaxSide with both sides multiples of K (the
+// positions per lane, lines_positions_per_lane).  Workspace layout, in
+// order: fp32 planes [nd][B][C][H*W], a 2 KiB sink for idle lanes' stores;
+// if LR or RL is enabled, x and lambda
+// transposed ([B][C][W][H], I/O dtype) and the enabled column directions'
+// raw taps transposed ([ncol][B][C/cpw][3][W][H]).
+constexpr int kLinesMaxSide = 512;
+struct LinesWorkspace {
+    float* planes;
+    float* sink;
+    void* xT;
+    void* lamT;
+    void* wT;
+};
+int lines_positions_per_lane(int H, int W);
+bool lines_supported(int H, int W);
+size_t lines_workspace_bytes(const ScanArgs& a);
+hipError_t launch_lines(const ScanArgs& a, void* workspace, hipStream_t stream);
+
+// Per-line fallback: any H, W <= 4096.  `planes` is an fp32 workspace of
 // popcount(dirs) * B*C*H*W floats.
 hipError_t launch_general(const ScanArgs& a, float* planes, hipStream_t stream);
 
