@@ -30,14 +30,37 @@ namespace {
 constexpr int kDepth = 4;   // lines prefetched ahead
 constexpr size_t kSinkBytes = 64 * 8 * sizeof(float);
 
+// 16-byte vector <-> floats
+__device__ __forceinline__ void unpack(uint4 r, float (&o)[8]) {
+    o[0] = bf16_lo(r.x); o[1] = bf16_hi(r.x); o[2] = bf16_lo(r.y); o[3] = bf16_hi(r.y);
+    o[4] = bf16_lo(r.z); o[5] = bf16_hi(r.z); o[6] = bf16_lo(r.w); o[7] = bf16_hi(r.w);
+}
+__device__ __forceinline__ void unpack(uint4 r, float (&o)[4]) {
+    o[0] = __uint_as_float(r.x); o[1] = __uint_as_float(r.y); o[2] = __uint_as_float(r.z); o[3] = __uint_as_float(r.w);
+}
+// non-temporal 16-byte store of 8 bf16 (rounded to nearest even) or 4 fp32
+__device__ __forceinline__ void store16_nt(uint16_t* p, const float (&v)[8]) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 r = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void store16_nt(float* p, const float (&v)[4]) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 r = {v[0], v[1], v[2], v[3]};
+    __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(p));
+}
+
 // ---------------------------------------------------------------- transpose
-// src [P][R][Cc] -> dst [P][Cc][R], one 64 x 64 tile per workgroup.
+// src [P][R][Cc] -> dst [P][Cc][R], one 64 x 64 tile per workgroup.  Whole
+// tiles move as 16-byte vectors (8 lanes per 128-byte row for bf16); a
+// tile that crosses the edge of the plane goes element by element.
 constexpr int kTile = 64;
 
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst, int R,
                                                         int Cc, int tiles_r, int tiles_c) {
-    __shared__ float tile[kTile][kTile + 1];   // values widened to fp32 (exact for bf16)
+    constexpr int N = 16 / sizeof(T);               // elements per 16-byte vector
+    __shared__ float tile[kTile][kTile + 1];        // values widened to fp32 (exact for bf16)
     const int t = blockIdx.x;
     const int tc = t % tiles_c;
     const int tr = (t / tiles_c) % tiles_r;
@@ -45,6 +68,38 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ sr
     const T* s = src + plane * (size_t)R * Cc;
     T* o = dst + plane * (size_t)R * Cc;
     const int r0 = tr * kTile, c0 = tc * kTile;
+    const bool whole = r0 + kTile <= R && c0 + kTile <= Cc && Cc % N == 0 && R % N == 0;
+    if (whole) {
+        // thread -> (row, vector) of the tile; then (column, vector of rows)
+        constexpr int kVPR = kTile / N;                       // vectors per tile row
+        constexpr int kIters = kTile * kVPR / 256;
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int v = threadIdx.x + 256 * it;
+            const int i = v / kVPR, cv = (v % kVPR) * N;
+            const uint4 raw = *reinterpret_cast<const uint4*>(s + (size_t)(r0 + i) * Cc + c0 + cv);
+            const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int e = 0; e < N; ++e) {
+                if constexpr (sizeof(T) == 2) tile[i][cv + e] = (e & 1) ? bf16_hi(wds[e >> 1]) : bf16_lo(wds[e >> 1]);
+                else tile[i][cv + e] = __uint_as_float(wds[e]);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int v = threadIdx.x + 256 * it;
+            const int cc = v / kVPR, rv = (v % kVPR) * N;    // output row cc, rows rv.. of the input
+            uint32_t wds[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (sizeof(T) == 2) wds[q] = pack_bf16x2(tile[rv + 2 * q][cc], tile[rv + 2 * q + 1][cc]);
+                else wds[q] = __float_as_uint(tile[rv + q][cc]);
+            }
+            *reinterpret_cast<uint4*>(o + (size_t)(c0 + cc) * R + r0 + rv) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+        }
+        return;
+    }
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     for (int i = ty; i < kTile; i += 4) {
         const int r = r0 + i, c = c0 + tx;
@@ -273,7 +328,9 @@ struct MergeParams {
 
 // y = u * (TB + BT + LR + RL) over one 64 x 64 tile of one (b, c) slice, in
 // that fixed order.  Row planes are [H][W]; column planes [W][H] are read
-// along their lines and transposed through LDS.
+// along their lines and transposed through LDS.  Thread -> (row, 16
+// consecutive columns): 16-byte accesses throughout; a tile that crosses the
+// edge of the slice goes element by element.
 template <typename T>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams prm) {
     __shared__ float tile[kTile][kTile + 1];
@@ -285,12 +342,71 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams prm) {
     const size_t HW = (size_t)H * W;
     const size_t E = (size_t)prm.B * prm.C * HW;
     const int r0 = tr * kTile, c0 = tc * kTile;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const T* __restrict__ gu = static_cast<const T*>(prm.u) + bc * HW;
+    T* __restrict__ gy = static_cast<T*>(prm.y) + bc * HW;
+    bool any_col = false;
+    for (int slot = 0; slot < prm.nd; ++slot) any_col |= prm.dir_of_slot[slot] >= 2;
 
+    if (r0 + kTile <= H && c0 + kTile <= W && W % 16 == 0 && H % 16 == 0) {
+        const int i = threadIdx.x >> 2, j0 = (threadIdx.x & 3) * 16;   // tile row i, columns j0..j0+15
+        float acc[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+        // column planes: tile[q][r] = sum over LR, RL (slot order) at
+        // (row r0 + r, column c0 + q); this thread reads line c0 + i
+        if (any_col) {
+            float cs[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) cs[e] = 0.0f;
+            for (int slot = 0; slot < prm.nd; ++slot) {
+                if (prm.dir_of_slot[slot] < 2) continue;
+                const float* P = prm.planes + slot * E + bc * HW + (size_t)(c0 + i) * H + r0 + j0;
+#pragma unroll
+                for (int e = 0; e < 16; e += 4) {
+                    const float4 v = *reinterpret_cast<const float4*>(P + e);
+                    cs[e] += v.x; cs[e + 1] += v.y; cs[e + 2] += v.z; cs[e + 3] += v.w;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) tile[i][j0 + e] = cs[e];
+        }
+        // row planes, in slot order (TB before BT)
+        for (int slot = 0; slot < prm.nd; ++slot) {
+            if (prm.dir_of_slot[slot] >= 2) continue;
+            const float* P = prm.planes + slot * E + bc * HW + (size_t)(r0 + i) * W + c0 + j0;
+#pragma unroll
+            for (int e = 0; e < 16; e += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(P + e);
+                acc[e] += v.x; acc[e + 1] += v.y; acc[e + 2] += v.z; acc[e + 3] += v.w;
+            }
+        }
+        __syncthreads();
+        const size_t o = (size_t)(r0 + i) * W + c0 + j0;
+        float uv[16], yv[16];
+#pragma unroll
+        for (int e = 0; e < 16; e += 16 / (int)sizeof(T) / 1) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(gu + o + e);
+            float f[16 / sizeof(T)];
+            unpack(raw, f);
+#pragma unroll
+            for (int q = 0; q < (int)(16 / sizeof(T)); ++q) uv[e + q] = f[q];
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) yv[e] = uv[e] * (any_col ? acc[e] + tile[j0 + e][i] : acc[e]);
+#pragma unroll
+        for (int e = 0; e < 16; e += 16 / (int)sizeof(T)) {
+            float f[16 / sizeof(T)];
+#pragma unroll
+            for (int q = 0; q < (int)(16 / sizeof(T)); ++q) f[q] = yv[e + q];
+            store16_nt(gy + o + e, f);
+        }
+        return;
+    }
+
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     float acc[kTile / 4];
 #pragma unroll
     for (int s = 0; s < kTile / 4; ++s) acc[s] = 0.0f;
-    // row planes, in slot order (TB before BT)
     for (int slot = 0; slot < prm.nd; ++slot) {
         if (prm.dir_of_slot[slot] >= 2) continue;
         const float* P = prm.planes + slot * E + bc * HW;
@@ -300,8 +416,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams prm) {
             if (r < H && q < W) acc[s] += P[(size_t)r * W + q];
         }
     }
-    // column planes: tile[q - c0][r - r0] = sum of LR, RL in slot order
-    bool any_col = false;
+    bool first = true;
     for (int slot = 0; slot < prm.nd; ++slot) {
         if (prm.dir_of_slot[slot] < 2) continue;
         const float* P = prm.planes + slot * E + bc * HW;
@@ -309,14 +424,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams prm) {
         for (int s = 0; s < kTile / 4; ++s) {
             const int q = c0 + ty + 4 * s, r = r0 + tx;
             const float v = (q < W && r < H) ? P[(size_t)q * H + r] : 0.0f;
-            if (any_col) tile[ty + 4 * s][tx] += v;
-            else tile[ty + 4 * s][tx] = v;
+            if (first) tile[ty + 4 * s][tx] = v;
+            else tile[ty + 4 * s][tx] += v;
         }
-        any_col = true;
+        first = false;
     }
     __syncthreads();
-    const T* __restrict__ gu = static_cast<const T*>(prm.u) + bc * HW;
-    T* __restrict__ gy = static_cast<T*>(prm.y) + bc * HW;
 #pragma unroll
     for (int s = 0; s < kTile / 4; ++s) {
         const int r = r0 + ty + 4 * s, q = c0 + tx;
