@@ -59,9 +59,15 @@
  * base pointers must be 16-byte aligned; y must not overlap any input.  Calls
  * only enqueue work on `stream` and never synchronise; a kernel fault shows
  * at the caller's next synchronisation.  Shapes with H <= 64 and W <= 64 run
- * one fused kernel and allocate nothing.  Larger shapes run the general path,
- * which takes an fp32 workspace of popcount(dirs) * B*C*H*W * 4 bytes
- * stream-ordered (hipMallocAsync / hipFreeAsync on `stream`).
+ * one fused kernel and allocate nothing.  Larger shapes run the general path
+ * and take a workspace stream-ordered (hipMallocAsync / hipFreeAsync on
+ * `stream`): with H, W <= 512 and both multiples of K (1, 2, 4 or 8 as
+ * max(H, W) is <= 64, 128, 256 or 512) the line kernels use
+ *   popcount(dirs) * B*C*H*W * 4 bytes (fp32 planes) + 2 KiB
+ *   + if LR or RL is enabled: (2 * B*C*H*W + ncol * B*(C/cpw)*3*H*W) * s
+ * (s = bytes per element, ncol = enabled column directions: transposed
+ * copies of x, lambda and their taps); other shapes use the per-line
+ * fallback with popcount(dirs) * B*C*H*W * 4 bytes.
  * The library keeps no other state: calls on different streams may run
  * concurrently.  Results are deterministic (fixed summation order, no atomics).
  *
@@ -113,7 +119,7 @@ enum {
 enum {
     GSPN_PATH_AUTO = 0,    /* what gspn_scan_fwd uses */
     GSPN_PATH_FUSED = 1,   /* one fused 4-direction kernel; needs H <= 64 and W <= 64 */
-    GSPN_PATH_GENERAL = 2  /* per-direction kernels + merge; any shape; uses a workspace */
+    GSPN_PATH_GENERAL = 2  /* line (or per-line) kernels + merge; any shape; uses a workspace */
 };
 
 /*
