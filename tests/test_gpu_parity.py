@@ -106,6 +106,15 @@ def test_edge_shapes_fused(case, dtype):
 
 
 EDGE_GENERAL = EDGE[:8] + [
+    # line kernels: K = 2, 4, 8 positions per lane, direction subsets, groups
+    (1, 2, 200, 136, 15, 1, 1),   # K = 4
+    (1, 2, 256, 32, 15, 8, 2),    # K = 4, local groups, shared weights
+    (1, 1, 320, 8, 15, 1, 1),     # K = 8, a very short side
+    (2, 2, 96, 128, 3, 1, 1),     # row directions only: no transposes
+    (2, 2, 128, 96, 12, 1, 1),    # column directions only
+    (1, 3, 128, 64, 6, 4, 3),     # BT + LR, groups, cpw 3
+    (1, 2, 512, 504, 15, 1, 1),   # K = 8, partial merge tiles
+    # per-line fallback
     (1, 2, 65, 65, 15, 1, 1),
     (1, 2, 100, 37, 15, 1, 1),
     (1, 2, 1, 300, 15, 1, 1),
