@@ -46,6 +46,9 @@ def open_library(path: str):
     lib.gspn_oracle_slice_f64.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_uint32, ctypes.c_int32]
     lib.gspn_oracle_slice_f64.restype = ctypes.c_int
+    lib.gspn_oracle_bwd_f64.argtypes = [dp] * 9 + [ctypes.c_int64] * 4 + [
+        ctypes.c_uint32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
+    lib.gspn_oracle_bwd_f64.restype = ctypes.c_int
     lib.gspn_oracle_max_threads.argtypes = []
     lib.gspn_oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -91,6 +94,30 @@ def scan_fwd(x, w, lam, u, *, dirs: int = 15, groups: int = 1, cpw: int = 1,
     if rc:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return y
+
+
+def scan_bwd(x, w, lam, u, gy, *, dirs: int = 15, groups: int = 1, cpw: int = 1,
+             nthreads: int = 0, lib=None):
+    """Gradients (gx, gw, glam, gu) in fp64 of L with dL/dy = gy.
+
+    Shapes as in scan_fwd; gw is dL/d(raw taps), shaped like w, with zeros on
+    the taps the forward never reads.
+    """
+    x, w, lam, u, gy = (_f64c(a) for a in (x, w, lam, u, gy))
+    B, C, H, W = x.shape
+    nd = bin(dirs & 15).count("1")
+    if lam.shape != x.shape or u.shape != x.shape or gy.shape != x.shape:
+        raise ValueError("x, lam, u, gy must share one shape")
+    if cpw < 1 or C % cpw or w.shape != (nd, B, C // cpw, 3, H, W):
+        raise ValueError(f"w has shape {w.shape}, expected {(nd, B, C // max(cpw, 1), 3, H, W)}")
+    gx, glam, gu = np.empty_like(x), np.empty_like(x), np.empty_like(x)
+    gw = np.empty_like(w)
+    rc = (lib or _load()).gspn_oracle_bwd_f64(
+        _dptr(x), _dptr(w), _dptr(lam), _dptr(u), _dptr(gy), _dptr(gx), _dptr(gw), _dptr(glam),
+        _dptr(gu), B, C, H, W, dirs, groups, cpw, nthreads)
+    if rc:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return gx, gw, glam, gu
 
 
 def slice_fwd(x, w, lam, u, *, dirs: int = 15, groups: int = 1) -> np.ndarray:

@@ -240,3 +240,240 @@ int gspn_oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------------
+ * Backward: the exact vector-Jacobian product of the forward above.
+ *
+ * The pages state only that a backward pass exists and runs about as fast
+ * as the forward ("GSPN-2" notes, implementation section); the gradients
+ * below are the chain rule applied to the forward's definition, written out
+ * step by step:
+ *
+ *   y = u * S,  S = sum_d h_d          =>  gu = gy * S,  gh = gy * u
+ *   h_i = w_i h_{i-1} + lam_i * x_i    =>  adjoint state, run from the last
+ *       line of a group back to its first:
+ *         g_i = gh_i + w_{i+1}^T g_{i+1}     (second term only when line i+1
+ *                                             is in the same group)
+ *       and, per direction, G = sum over that direction's g at each pixel:
+ *         gx  += lam * g,  glam += x * g
+ *         dL/dw_t[i][p] = g_i[p] * h_{i-1}[p+t-1]   (valid taps, i not a
+ *                                                    group's first line)
+ *   w_t = s_t / sum_v s_v, s = sigmoid(a)  =>
+ *         ga_t = s_t (1 - s_t) / sum_v s_v * (dw_t - sum_v dw_v w_v)
+ *       for valid taps; unused taps (missing neighbours, first lines of
+ *       groups) get 0.  dw is summed over the cpw channels sharing the set
+ *       before this step (the step is linear in dw).
+ * ---------------------------------------------------------------------- */
+
+/* Normalised weights and sigmoids of pixel p of line i (direction d), valid
+ * taps only; invalid taps get w = s = 0.  Returns the sigmoid sum. */
+static double line_taps(const double *wd, int d, int64_t H, int64_t W, int64_t i, int64_t p,
+                        int64_t m, double wt[3], double st[3])
+{
+    const int64_t HW = H * W;
+    int64_t r, q;
+    pixel_of(d, H, W, i, p, &r, &q);
+    double ssum = 0.0;
+    for (int t = 0; t < 3; ++t) {
+        const int64_t pp = p + t - 1;
+        st[t] = 0.0;
+        if (pp < 0 || pp >= m)
+            continue;
+        st[t] = sigmoid(wd[(int64_t)t * HW + r * W + q]);
+        ssum += st[t];
+    }
+    for (int t = 0; t < 3; ++t)
+        wt[t] = st[t] / ssum;
+    return ssum;
+}
+
+/*
+ * One weight set (b, k) and its cpw channels, one direction at a time.
+ *   x, lam, u, gy, gx, glam, gu : [cpw][H][W] (this set's channels)
+ *   w, gw : [popcount(dirs)][3][H][W] (this set's slabs; gw written fully)
+ *   work  : H*W (forward states) + 2*max(H,W) + 2*H*W doubles
+ */
+static int set_bwd(const double *x, const double *w, const double *lam, const double *u,
+                   const double *gy, double *gx, double *gw, double *glam, double *gu,
+                   int64_t H, int64_t W, uint32_t dirs, int32_t groups, int32_t cpw, double *work)
+{
+    const int64_t HW = H * W;
+    const int64_t mmax = H > W ? H : W;
+    double *hist = work;              /* [n][m] forward states of one direction */
+    double *g = work + HW;            /* adjoint of line i */
+    double *gn = g + mmax;            /* adjoint of line i + 1 */
+    double *G = gn + mmax;            /* [H][W] sum over directions of the adjoint */
+    double *S = G + HW;               /* [H][W] sum over directions of h */
+    const int nd = ndirs_of(dirs);
+    memset(gw, 0, sizeof(double) * (size_t)(nd * 3 * HW));
+
+    for (int32_t c = 0; c < cpw; ++c) {
+        const double *xc = x + c * HW, *lc = lam + c * HW, *uc = u + c * HW, *gyc = gy + c * HW;
+        memset(G, 0, sizeof(double) * (size_t)HW);
+        memset(S, 0, sizeof(double) * (size_t)HW);
+        int slab = 0;
+        for (int d = 0; d < 4; ++d) {
+            if (!((dirs >> d) & 1u))
+                continue;
+            const double *wd = w + (int64_t)slab * 3 * HW;
+            double *gwd = gw + (int64_t)slab * 3 * HW;
+            ++slab;
+            const int64_t n = (d == DIR_TB || d == DIR_BT) ? H : W;
+            const int64_t m = (d == DIR_TB || d == DIR_BT) ? W : H;
+            if (n % groups)
+                return -1;
+            const int64_t L = n / groups;
+            double wt[3], st[3];
+
+            /* forward, keeping every line's state */
+            for (int64_t i = 0; i < n; ++i) {
+                for (int64_t p = 0; p < m; ++p) {
+                    int64_t r, q;
+                    pixel_of(d, H, W, i, p, &r, &q);
+                    double v = lc[r * W + q] * xc[r * W + q];
+                    if (i % L != 0) {
+                        line_taps(wd, d, H, W, i, p, m, wt, st);
+                        for (int t = 0; t < 3; ++t) {
+                            const int64_t pp = p + t - 1;
+                            if (pp >= 0 && pp < m)
+                                v += wt[t] * hist[(i - 1) * m + pp];
+                        }
+                    }
+                    hist[i * m + p] = v;
+                    S[r * W + q] += v;
+                }
+            }
+
+            /* adjoint, last line first */
+            for (int64_t i = n - 1; i >= 0; --i) {
+                for (int64_t p = 0; p < m; ++p) {
+                    int64_t r, q;
+                    pixel_of(d, H, W, i, p, &r, &q);
+                    g[p] = gyc[r * W + q] * uc[r * W + q];
+                }
+                if (i + 1 < n && (i + 1) % L != 0) {
+                    /* + w_{i+1}^T g_{i+1}: pixel p' of line i+1 reads p'+t-1 */
+                    for (int64_t pq = 0; pq < m; ++pq) {
+                        line_taps(wd, d, H, W, i + 1, pq, m, wt, st);
+                        for (int t = 0; t < 3; ++t) {
+                            const int64_t pp = pq + t - 1;
+                            if (pp >= 0 && pp < m)
+                                g[pp] += wt[t] * gn[pq];
+                        }
+                    }
+                }
+                for (int64_t p = 0; p < m; ++p) {
+                    int64_t r, q;
+                    pixel_of(d, H, W, i, p, &r, &q);
+                    G[r * W + q] += g[p];
+                    if (i % L != 0) {
+                        for (int t = 0; t < 3; ++t) {
+                            const int64_t pp = p + t - 1;
+                            if (pp < 0 || pp >= m)
+                                continue;
+                            gwd[(int64_t)t * HW + r * W + q] += g[p] * hist[(i - 1) * m + pp];
+                        }
+                    }
+                }
+                memcpy(gn, g, sizeof(double) * (size_t)m);
+            }
+        }
+        for (int64_t j = 0; j < HW; ++j) {
+            gx[c * HW + j] = lc[j] * G[j];
+            glam[c * HW + j] = xc[j] * G[j];
+            gu[c * HW + j] = gyc[j] * S[j];
+        }
+    }
+
+    /* through sigmoid-then-normalise: dL/dw -> dL/da, in place */
+    int slab = 0;
+    for (int d = 0; d < 4; ++d) {
+        if (!((dirs >> d) & 1u))
+            continue;
+        const double *wd = w + (int64_t)slab * 3 * HW;
+        double *gwd = gw + (int64_t)slab * 3 * HW;
+        ++slab;
+        const int64_t n = (d == DIR_TB || d == DIR_BT) ? H : W;
+        const int64_t m = (d == DIR_TB || d == DIR_BT) ? W : H;
+        const int64_t L = n / groups;
+        for (int64_t i = 0; i < n; ++i) {
+            for (int64_t p = 0; p < m; ++p) {
+                int64_t r, q;
+                pixel_of(d, H, W, i, p, &r, &q);
+                double *gp[3];
+                for (int t = 0; t < 3; ++t)
+                    gp[t] = gwd + (int64_t)t * HW + r * W + q;
+                if (i % L == 0) {
+                    for (int t = 0; t < 3; ++t)
+                        *gp[t] = 0.0;
+                    continue;
+                }
+                double wt[3], st[3];
+                const double ssum = line_taps(wd, d, H, W, i, p, m, wt, st);
+                double dot = 0.0;
+                for (int t = 0; t < 3; ++t)
+                    dot += *gp[t] * wt[t];
+                for (int t = 0; t < 3; ++t)
+                    *gp[t] = st[t] * (1.0 - st[t]) / ssum * (*gp[t] - dot);
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Whole tensors, same layouts as gspn_oracle_fwd_f64; gy is dL/dy.
+ * Outputs gx, glam, gu : [B][C][H][W] and gw : [popcount(dirs)][B][C/cpw][3][H][W]
+ * (dL/d raw taps), all fully written.  OpenMP over weight sets (b, k).
+ */
+int gspn_oracle_bwd_f64(const double *x, const double *w, const double *lam, const double *u,
+                        const double *gy, double *gx, double *gw, double *glam, double *gu,
+                        int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs,
+                        int32_t groups, int32_t cpw, int nthreads)
+{
+    int rc = check_args(B, C, H, W, dirs, groups, cpw);
+    if (rc)
+        return rc;
+    if (!x || !w || !lam || !u || !gy || !gx || !gw || !glam || !gu)
+        return -1;
+    const int64_t HW = H * W;
+    const int64_t Cw = C / cpw;
+    const int nd = ndirs_of(dirs);
+    const int64_t mmax = H > W ? H : W;
+    const int64_t nsets = B * Cw;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel reduction(| : bad)
+    {
+        double *work = (double *)malloc(sizeof(double) * (size_t)(3 * HW + 2 * mmax));
+        double *wsl = (double *)malloc(sizeof(double) * (size_t)(2 * nd * 3 * HW));
+        if (!work || !wsl) {
+            bad = 1;
+        } else {
+            double *gsl = wsl + (int64_t)nd * 3 * HW;
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t s = 0; s < nsets; ++s) {
+                const int64_t b = s / Cw, k = s % Cw;
+                for (int j = 0; j < nd; ++j)
+                    memcpy(wsl + (int64_t)j * 3 * HW,
+                           w + (((int64_t)j * B + b) * Cw + k) * 3 * HW,
+                           sizeof(double) * (size_t)(3 * HW));
+                const int64_t off = (b * C + k * cpw) * HW;
+                if (set_bwd(x + off, wsl, lam + off, u + off, gy + off, gx + off, gsl,
+                            glam + off, gu + off, H, W, dirs, groups, cpw, work))
+                    bad = 1;
+                for (int j = 0; j < nd; ++j)
+                    memcpy(gw + (((int64_t)j * B + b) * Cw + k) * 3 * HW,
+                           gsl + (int64_t)j * 3 * HW, sizeof(double) * (size_t)(3 * HW));
+            }
+        }
+        free(work);
+        free(wsl);
+    }
+    return bad ? -2 : 0;
+}

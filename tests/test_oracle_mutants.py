@@ -43,6 +43,23 @@ MUTANTS = {
     "tap_index_swapped": [("s[t] = sigmoid(wd[(int64_t)t * HW", "s[t] = sigmoid(wd[(int64_t)(2 - t) * HW")],
 }
 
+# Mistakes planted in the backward pass; the forward pins above cannot see them.
+BWD_MUTANTS = {
+    "bwd_no_carry": [("g[pp] += wt[t] * gn[pq];", "(void)gn;")],
+    "bwd_carry_not_transposed": [("g[pp] += wt[t] * gn[pq];", "g[pq] += wt[t] * gn[pp];")],
+    "bwd_carry_across_groups": [("if (i + 1 < n && (i + 1) % L != 0) {", "if (i + 1 < n) {")],
+    "bwd_carry_uses_own_line_weights": [("line_taps(wd, d, H, W, i + 1, pq, m, wt, st);",
+                                         "line_taps(wd, d, H, W, i, pq, m, wt, st);")],
+    "bwd_no_normalise_coupling": [("(*gp[t] - dot)", "(*gp[t])")],
+    "bwd_no_sigmoid_slope": [("st[t] * (1.0 - st[t]) / ssum", "st[t] / ssum")],
+    "bwd_gx_uses_x": [("gx[c * HW + j] = lc[j] * G[j];", "gx[c * HW + j] = xc[j] * G[j];")],
+    "bwd_gu_last_direction_only": [("S[r * W + q] += v;", "S[r * W + q] = v;")],
+    "bwd_tap_grad_uses_current_line": [("g[p] * hist[(i - 1) * m + pp]", "g[p] * hist[i * m + pp]")],
+    "bwd_gate_not_applied": [("g[p] = gyc[r * W + q] * uc[r * W + q];", "g[p] = gyc[r * W + q];")],
+    "bwd_tap_grad_not_summed_over_channels": [
+        ("gwd[(int64_t)t * HW + r * W + q] += g[p]", "gwd[(int64_t)t * HW + r * W + q] = g[p]")],
+}
+
 
 def _build(tmp_path, name, edits):
     src = open(SRC).read()
@@ -95,11 +112,59 @@ def _pin_failures(lib):
     return failed
 
 
+def _bwd_pin_failures(lib):
+    """Backward pins: directional derivatives of the dense closed form, the
+    exact linear identities for x / lambda / u, zero tap gradient on ones."""
+    failed = []
+    rng = np.random.default_rng(4321)
+
+    def loss(x, w, lam, u, gy, **kw):
+        return float((bruteforce_fwd(x, w, lam, u, check=False, **kw) * gy).sum())
+
+    for (H, W, g, cpw) in [(5, 4, 1, 1), (6, 4, 2, 2)]:
+        B, C = 1, 4
+        kw = dict(groups=g, cpw=cpw)
+        x = rng.standard_normal((B, C, H, W))
+        lam = rng.random((B, C, H, W))
+        u = rng.random((B, C, H, W))
+        gy = rng.standard_normal((B, C, H, W))
+        w = rng.standard_normal((4, B, C // cpw, 3, H, W))
+        gx, gw, glam, gu = oracle.scan_bwd(x, w, lam, u, gy, lib=lib, **kw)
+        if not all(np.all(np.isfinite(a)) for a in (gx, gw, glam, gu)):
+            failed.append(f"finite{H}x{W}")
+            continue
+        v = rng.standard_normal(w.shape)
+        eps = 1e-5
+        fd = (loss(x, w + eps * v, lam, u, gy, **kw) - loss(x, w - eps * v, lam, u, gy, **kw)) / (2 * eps)
+        if abs(float((gw * v).sum()) - fd) > 1e-7 * max(1.0, abs(fd)):
+            failed.append(f"tap_fd{H}x{W}g{g}c{cpw}")
+        v = rng.standard_normal(x.shape)
+        for name, got, args in (("x", gx, (v, w, lam, u)), ("lam", glam, (x, w, v, u)),
+                                ("u", gu, (x, w, lam, v))):
+            want = loss(*args, gy, **kw)
+            if abs(float((got * v).sum()) - want) > 1e-10 * max(1.0, abs(want)):
+                failed.append(f"linear_{name}{H}x{W}g{g}c{cpw}")
+    one = np.ones((1, 2, 6, 5))
+    gw = oracle.scan_bwd(one, 2 * rng.standard_normal((4, 1, 2, 3, 6, 5)), one, one,
+                         rng.standard_normal(one.shape), lib=lib)[1]
+    if np.abs(gw).max() > 1e-11:
+        failed.append("ones_zero_tap_grad")
+    return failed
+
+
 def test_unmodified_oracle_passes_every_pin(tmp_path):
-    assert _pin_failures(_build(tmp_path, "original", [])) == []
+    lib = _build(tmp_path, "original", [])
+    assert _pin_failures(lib) == []
+    assert _bwd_pin_failures(lib) == []
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(tmp_path, name):
     failed = _pin_failures(_build(tmp_path, name, MUTANTS[name]))
     assert failed, f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(tmp_path, name):
+    failed = _bwd_pin_failures(_build(tmp_path, name, BWD_MUTANTS[name]))
+    assert failed, f"mutant {name} passed every backward pin"
