@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the GSPN 4-direction line-scan forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config cgspn1k]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config cgspn1k] [--pass fwd|bwd]
 
 One step = one call of gspn_scan_fwd (the whole forward: weight
 normalisation, the four directional scans, merge and store) over one batch
@@ -22,6 +22,14 @@ bytes count each input once, y once, and only the taps the method consumes:
     s * (|x| + |lam| + |u| + |y|) + s * B * Cw * sum_d (n_d - g) * (3 m_d - 2)
 (group-start lines and taps past a line border are never read).
 
+With --pass bwd a step is one call of gspn_scan_bwd instead (the backward:
+forward states recomputed, adjoint scans, all four gradients), and its
+algorithmic bytes are the inputs x, lam, u, gy once, the taps the forward
+consumes, gx, glam, gu once and the whole tap-gradient tensor once:
+    s * (4 + 3) * |x| + s * B * Cw * sum_d (n_d - g) * (3 m_d - 2)
+    + s * ndir * B * Cw * 3 * H * W.
+Its roofline object covers the whole call (all of its launches).
+
 Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -37,6 +45,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GSPN scan GB/s and % of HBM peak (4-dir fwd), 1K C-GSPN config"
+METRIC_BWD = "GSPN scan backward GB/s and % of HBM peak (4-dir bwd)"
 HBM_PEAK_GBPS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fused_scan_kernel_cgspn1k_traffic.txt")
 PROFILE_STATS = os.path.join(ROOT, "profiles", "fused_scan_kernel_cgspn1k_stats.txt")
@@ -55,6 +64,14 @@ def algorithmic_bytes(B, C, H, W, dirs, groups, cpw, dtype) -> int:
             n, m = (H, W) if d < 2 else (W, H)
             total += s * B * Cw * (n - groups) * max(3 * m - 2, 1 if m == 1 else 0)
     return total
+
+
+def algorithmic_bytes_bwd(B, C, H, W, dirs, groups, cpw, dtype) -> int:
+    s = 2 if dtype == "bf16" else 4
+    E = B * C * H * W
+    nd = bin(dirs & 15).count("1")
+    fwd_taps = algorithmic_bytes(B, C, H, W, dirs, groups, cpw, dtype) - 4 * E * s
+    return 7 * E * s + fwd_taps + s * nd * B * (C // cpw) * 3 * H * W
 
 
 def kernel_source_hash() -> str:
@@ -178,11 +195,11 @@ def summarize_stats(stats_csv, command, config="cgspn1k"):
     print("\n".join(lines))
 
 
-def cpu_baseline(cfg_name: str, budget_s: float = 8.0):
+def cpu_baseline(cfg_name: str, budget_s: float = 8.0, backward: bool = False):
     """Time the fp64 oracle on a bounded sample of the same workload: whole
     batch items, repeated until about budget_s seconds of wall time."""
     import oracle
-    from linear_spatial_propagation_amd.inputs import CONFIGS, make_workload
+    from linear_spatial_propagation_amd.inputs import CONFIGS, gy_f64, make_gy, make_workload
 
     cfg = dict(CONFIGS[cfg_name])
     B = cfg.pop("B")
@@ -191,11 +208,15 @@ def cpu_baseline(cfg_name: str, budget_s: float = 8.0):
 
     def prepare(nb):
         wl = make_workload(nb, C, H, W, **cfg)
-        return wl, (wl.x, wl.w, wl.lam, wl.u)
+        args = (wl.x, wl.w, wl.lam, wl.u)
+        if backward:
+            args += (gy_f64(make_gy(wl, 1000 + cfg["seed"]), wl.dtype),)
+        return wl, args
 
     def run(wl, args):
         t0 = time.perf_counter()
-        oracle.scan_fwd(*args, dirs=15, groups=wl.groups, cpw=wl.cpw, nthreads=threads)
+        fn = oracle.scan_bwd if backward else oracle.scan_fwd
+        fn(*args, dirs=15, groups=wl.groups, cpw=wl.cpw, nthreads=threads)
         return time.perf_counter() - t0
 
     wl, args = prepare(1)
@@ -208,7 +229,8 @@ def cpu_baseline(cfg_name: str, budget_s: float = 8.0):
         total += run(wl, args)
         reps += 1
     t = total / reps
-    nbytes = algorithmic_bytes(nb, C, H, W, 15, cfg["groups"], cfg["cpw"], cfg["dtype"])
+    nbytes = (algorithmic_bytes_bwd if backward else algorithmic_bytes)(
+        nb, C, H, W, 15, cfg["groups"], cfg["cpw"], cfg["dtype"])
     return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{nb} of {B} batch items ({nb * C} (b,c) slices) of the same workload, "
                       f"fp64 C oracle with OpenMP over slices, mean of {reps} runs of {t:.3f} s"}
@@ -220,6 +242,8 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="cgspn1k")
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the backward")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for counter calibration)")
@@ -257,19 +281,30 @@ def main():
         t = torch.from_numpy(np.ascontiguousarray(a))
         return (t.view(torch.bfloat16) if wl.dtype == "bf16" else t).to(dev)
 
+    bwd = args.pass_ == "bwd"
     base = [up(a) for a in (wl.x_store, wl.w_store, wl.lam_store, wl.u_store)]
-    nbytes = algorithmic_bytes(B, C, H, W, 15, wl.groups, wl.cpw, wl.dtype)
-    footprint = sum(t.numel() * t.element_size() for t in base) + base[0].numel() * base[0].element_size()
+    if bwd:
+        from linear_spatial_propagation_amd.inputs import make_gy
+        base.append(up(make_gy(wl, 1000 + cfgd["seed"])))
+        nbytes = algorithmic_bytes_bwd(B, C, H, W, 15, wl.groups, wl.cpw, wl.dtype)
+        outs_like = [base[0], base[1], base[0], base[0]]
+    else:
+        nbytes = algorithmic_bytes(B, C, H, W, 15, wl.groups, wl.cpw, wl.dtype)
+        outs_like = [base[0]]
+    footprint = sum(t.numel() * t.element_size() for t in base + outs_like)
     R = max(1, -(-512 * 1024 * 1024 // footprint))
     sets = []
     for r in range(R):
         ins = [t.clone() for t in base] if r else base
-        sets.append((ins, torch.empty_like(base[0])))
+        sets.append((ins, [torch.empty_like(t) for t in outs_like]))
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
-        ins, y = sets[i % R]
-        gspn.scan_fwd(*ins, dirs=15, groups=wl.groups, ch_per_weight=wl.cpw, out=y)
+        ins, outs = sets[i % R]
+        if bwd:
+            gspn.scan_bwd(*ins, dirs=15, groups=wl.groups, ch_per_weight=wl.cpw, out=outs)
+        else:
+            gspn.scan_fwd(*ins, dirs=15, groups=wl.groups, ch_per_weight=wl.cpw, out=outs[0])
 
     for i in range(args.warmup):
         step(i)
@@ -313,10 +348,10 @@ def main():
     value = nbytes * args.steps / elapsed / 1e9
     avg_launch = float(per.mean())
     achieved = nbytes / avg_launch / 1e9
-    traffic = load_traffic() if args.config == "cgspn1k" else None
+    traffic = load_traffic() if args.config == "cgspn1k" and not bwd else None
     E = B * C * H * W
     out = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if bwd else METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -332,8 +367,9 @@ def main():
             "workload": f"{args.config}: B={B} C={C} H={H} W={W} groups={wl.groups} "
                         f"ch_per_weight={wl.cpw} dirs=TB|BT|LR|RL, {wl.dtype} I/O, fp32 arithmetic",
             "io_dtype": wl.dtype,
-            "path": {1: "fused", 2: "general"}[gspn.select_path(B, C, H, W, groups=wl.groups,
-                                                                 ch_per_weight=wl.cpw)],
+            "path": "backward line kernels" if bwd else
+                    {1: "fused", 2: "general"}[gspn.select_path(B, C, H, W, groups=wl.groups,
+                                                                ch_per_weight=wl.cpw)],
             "algorithmic_bytes_per_step": nbytes,
             "buffer_sets": R,
             "seed": cfgd["seed"],
@@ -348,8 +384,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
     }
+    if bwd:
+        out["roofline"]["kernel"] = "gspn_scan_bwd, all launches of one call"
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(args.config)
+        out["cpu_baseline"] = cpu_baseline(args.config, backward=bwd)
     print(json.dumps(out), flush=True)
 
 

@@ -107,9 +107,9 @@ enum {
     GSPN_ERR_CPW = -5,    /* ch_per_weight < 1 or it does not divide C */
     GSPN_ERR_DTYPE = -6,  /* unknown dtype */
     GSPN_ERR_ALIGN = -7,  /* a base pointer is not 16-byte aligned */
-    GSPN_ERR_ALIAS = -8,  /* y overlaps an input */
+    GSPN_ERR_ALIAS = -8,  /* an output overlaps an input or another output */
     GSPN_ERR_HIP = -9,    /* a HIP call failed; see gspn_last_error() */
-    GSPN_ERR_PATH = -10   /* unknown path, or the forced path cannot take this shape */
+    GSPN_ERR_PATH = -10   /* unknown path, or the path (or the backward) cannot take this shape */
 };
 
 /* Largest H and W accepted. */
@@ -150,6 +150,51 @@ int gspn_scan_fwd_path(const void *x, const void *w_raw, const void *lam, const 
  * GSPN_PATH_GENERAL), or a negative error code for invalid sizes. */
 int gspn_select_path(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
                      int32_t ch_per_weight, int32_t dtype);
+
+/*
+ * Backward of gspn_scan_fwd: the exact vector-Jacobian product of the
+ * definition above for a loss L with dL/dy = gy.  The pages give no formulas
+ * for it ("GSPN-2: Efficient Parallel Sequence Modeling", author response,
+ * "How Channel-shared Weight Mitigates the Concurrency Bottleneck?", states
+ * only that the backward gains as much as the forward); with
+ * S = sum over enabled d of h_d and g_d the adjoint state of direction d:
+ *   gu   = gy * S
+ *   g_d  : for the lines of each group from its last line back to its first,
+ *          g_i = gy * u (at line i) + w_{i+1}^T g_{i+1}, the second term only
+ *          when line i+1 is in the same group;
+ *          (w^T g)[p] = w_0[p+1] g[p+1] + w_1[p] g[p] + w_2[p-1] g[p-1]
+ *   gx   = lam * sum_d g_d,   glam = x * sum_d g_d
+ *   gw_raw[slab(d)][b][k][t][pixel of (i, p)] = w_t (1 - sigmoid(a_t))
+ *          (D_t - sum_v D_v w_v),  D_t = sum over the channels c of weight
+ *          set k of g_i[p] h_{i-1}[p+t-1],
+ *          for the taps the forward reads, and 0 for every other tap
+ *          (missing border neighbours, first lines of groups, lines of
+ *          length 1).
+ *   x, w_raw, lam, u, gy : inputs, layouts and dtype as in gspn_scan_fwd
+ *   gx, glam, gu : [B][C][H][W] outputs;  gw_raw : layout of w_raw (output)
+ * All four outputs are fully overwritten and must not overlap each other or
+ * an input (GSPN_ERR_ALIAS).  Arithmetic in fp32, outputs rounded to the
+ * dtype with round-to-nearest-even; tap gradients are summed over a set's
+ * channels in a fixed order (deterministic).
+ * Shapes: H, W <= 512 and both multiples of K (as for the forward's line
+ * kernels), else GSPN_ERR_PATH; gspn_bwd_supported tells in advance.
+ * Workspace, taken stream-ordered on `stream` (hipMallocAsync/hipFreeAsync),
+ * each part rounded up to 256 bytes:
+ *   popcount(dirs) * B*C*H*W * 4 (fp32 states, then adjoints) + 2 KiB
+ *   + popcount(dirs) * B*(C/cpw)*3*H*W * 4 (fp32 tap gradients)
+ *   + if LR or RL is enabled: (4 * B*C*H*W + ncol * B*(C/cpw)*3*H*W) * s
+ *     (transposed x, lam, gy, u and column-direction taps).
+ * Enqueues only; never synchronises.
+ */
+int gspn_scan_bwd(const void *x, const void *w_raw, const void *lam, const void *u, const void *gy,
+                  void *gx, void *gw_raw, void *glam, void *gu, int64_t B, int64_t C, int64_t H,
+                  int64_t W, uint32_t dirs, int32_t groups, int32_t ch_per_weight, int32_t dtype,
+                  hipStream_t stream);
+
+/* GSPN_OK if gspn_scan_bwd can run these sizes, GSPN_ERR_PATH if the shape is
+ * outside its kernels, or another negative code for invalid sizes. */
+int gspn_bwd_supported(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
+                       int32_t ch_per_weight, int32_t dtype);
 
 /* Static text for a status code. */
 const char *gspn_status_string(int status);

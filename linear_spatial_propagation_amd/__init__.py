@@ -1,6 +1,7 @@
 """GSPN 2D line-scan propagation on MI355X (gfx950).
 
     y = scan_fwd(x, w_raw, lam, u, dirs=15, groups=1, ch_per_weight=1)
+    gx, gw_raw, glam, gu = scan_bwd(x, w_raw, lam, u, gy, dirs=15, groups=1, ch_per_weight=1)
 
 computes the 4-direction line recurrence of the Generalized Spatial
 Propagation Network with hand-written HIP kernels (libgspn.so, C ABI in
@@ -17,7 +18,7 @@ from . import _lib
 from ._lib import (DIR_ALL, DIR_BT, DIR_LR, DIR_RL, DIR_TB, PATH_AUTO, PATH_FUSED, PATH_GENERAL,
                    GspnError, load, select_path)
 
-__all__ = ["scan_fwd", "select_path", "load", "GspnError", "DIR_TB", "DIR_BT", "DIR_LR", "DIR_RL",
+__all__ = ["scan_fwd", "scan_bwd", "select_path", "load", "GspnError", "DIR_TB", "DIR_BT", "DIR_LR", "DIR_RL",
            "DIR_ALL", "PATH_AUTO", "PATH_FUSED", "PATH_GENERAL"]
 
 
@@ -30,11 +31,8 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
 
 
-def scan_fwd(x, w_raw, lam, u, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1,
-             out=None, path: int = PATH_AUTO):
-    """Forward GSPN scan on the current HIP stream; returns y [B, C, H, W]."""
-    import torch
-    tensors = {"x": x, "w_raw": w_raw, "lam": lam, "u": u}
+def _check_inputs(tensors, dirs, ch_per_weight):
+    x = tensors["x"]
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU (HIP) device")
@@ -49,13 +47,53 @@ def scan_fwd(x, w_raw, lam, u, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_w
         raise ValueError("x must be [B, C, H, W]")
     B, C, H, W = x.shape
     nd = bin(dirs & 15).count("1")
-    if lam.shape != x.shape or u.shape != x.shape:
-        raise ValueError("lam and u must have x's shape")
+    for name, t in tensors.items():
+        if name != "w_raw" and t.shape != x.shape:
+            raise ValueError(f"{name} must have x's shape")
     if ch_per_weight < 1 or C % ch_per_weight:
         raise ValueError("ch_per_weight must divide C")
+    w_raw = tensors["w_raw"]
     if tuple(w_raw.shape) != (nd, B, C // ch_per_weight, 3, H, W):
         raise ValueError(f"w_raw has shape {tuple(w_raw.shape)}, expected "
                          f"{(nd, B, C // ch_per_weight, 3, H, W)}")
+    return dev, (B, C, H, W)
+
+
+def scan_bwd(x, w_raw, lam, u, gy, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1,
+             out=None):
+    """Backward GSPN scan on the current HIP stream.
+
+    Returns (gx, gw_raw, glam, gu), the gradients of a loss whose gradient
+    with respect to y = scan_fwd(x, w_raw, lam, u) is gy.  ``out`` may give
+    the four output tensors (contiguous, shaped like x, w_raw, x, x).
+    """
+    import torch
+    dev, (B, C, H, W) = _check_inputs({"x": x, "w_raw": w_raw, "lam": lam, "u": u, "gy": gy},
+                                      dirs, ch_per_weight)
+    if out is None:
+        gx, glam, gu = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+        gw = torch.empty_like(w_raw)
+    else:
+        gx, gw, glam, gu = out
+        for t, like in ((gx, x), (gw, w_raw), (glam, x), (gu, x)):
+            if (t.shape != like.shape or t.dtype != like.dtype or t.device != dev
+                    or not t.is_contiguous()):
+                raise ValueError("out tensors must be contiguous and shaped like x, w_raw, x, x")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = _lib.scan_bwd_ptr(x.data_ptr(), w_raw.data_ptr(), lam.data_ptr(), u.data_ptr(),
+                               gy.data_ptr(), gx.data_ptr(), gw.data_ptr(), glam.data_ptr(),
+                               gu.data_ptr(), B, C, H, W, dirs=dirs, groups=groups,
+                               ch_per_weight=ch_per_weight, dtype=_dtype_code(x), stream=stream)
+    _lib.check(rc)
+    return gx, gw, glam, gu
+
+
+def scan_fwd(x, w_raw, lam, u, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1,
+             out=None, path: int = PATH_AUTO):
+    """Forward GSPN scan on the current HIP stream; returns y [B, C, H, W]."""
+    import torch
+    dev, (B, C, H, W) = _check_inputs({"x": x, "w_raw": w_raw, "lam": lam, "u": u}, dirs, ch_per_weight)
     if out is None:
         out = torch.empty_like(x)
     elif out.shape != x.shape or out.dtype != x.dtype or out.device != dev or not out.is_contiguous():

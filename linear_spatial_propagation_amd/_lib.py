@@ -20,8 +20,8 @@ PATH_FUSED = 1
 PATH_GENERAL = 2
 DIR_TB, DIR_BT, DIR_LR, DIR_RL, DIR_ALL = 1, 2, 4, 8, 15
 
-EXPORTED = ("gspn_scan_fwd", "gspn_scan_fwd_path", "gspn_select_path", "gspn_status_string",
-            "gspn_last_error", "gspn_version")
+EXPORTED = ("gspn_scan_fwd", "gspn_scan_fwd_path", "gspn_select_path", "gspn_scan_bwd",
+            "gspn_bwd_supported", "gspn_status_string", "gspn_last_error", "gspn_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -51,6 +51,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.gspn_scan_fwd_path.restype = ctypes.c_int
         lib.gspn_select_path.argtypes = [i64, i64, i64, i64, u32, i32, i32, i32]
         lib.gspn_select_path.restype = ctypes.c_int
+        lib.gspn_scan_bwd.argtypes = [vp] * 9 + [i64, i64, i64, i64, u32, i32, i32, i32, vp]
+        lib.gspn_scan_bwd.restype = ctypes.c_int
+        lib.gspn_bwd_supported.argtypes = [i64, i64, i64, i64, u32, i32, i32, i32]
+        lib.gspn_bwd_supported.restype = ctypes.c_int
         lib.gspn_status_string.argtypes = [ctypes.c_int]
         lib.gspn_status_string.restype = ctypes.c_char_p
         lib.gspn_last_error.argtypes = []
@@ -79,6 +83,18 @@ def scan_fwd_ptr(x: int, w: int, lam: int, u: int, y: int, B: int, C: int, H: in
     """Raw call on device pointers; returns the status code."""
     return load().gspn_scan_fwd_path(x, w, lam, u, y, B, C, H, W, dirs, groups, ch_per_weight,
                                      dtype, path, stream)
+
+
+def scan_bwd_ptr(x: int, w: int, lam: int, u: int, gy: int, gx: int, gw: int, glam: int, gu: int,
+                 B: int, C: int, H: int, W: int, *, dirs: int = DIR_ALL, groups: int = 1,
+                 ch_per_weight: int = 1, dtype: int = GSPN_BF16, stream: int = 0) -> int:
+    """Raw backward call on device pointers; returns the status code."""
+    return load().gspn_scan_bwd(x, w, lam, u, gy, gx, gw, glam, gu, B, C, H, W, dirs, groups,
+                                ch_per_weight, dtype, stream)
+
+
+def bwd_supported(B, C, H, W, *, dirs=DIR_ALL, groups=1, ch_per_weight=1, dtype=GSPN_BF16) -> int:
+    return load().gspn_bwd_supported(B, C, H, W, dirs, groups, ch_per_weight, dtype)
 
 
 def select_path(B, C, H, W, *, dirs=DIR_ALL, groups=1, ch_per_weight=1, dtype=GSPN_BF16) -> int:

@@ -66,7 +66,7 @@ const char* gspn_status_string(int status) {
         case GSPN_ERR_CPW: return "GSPN_ERR_CPW: ch_per_weight must be >= 1 and divide C";
         case GSPN_ERR_DTYPE: return "GSPN_ERR_DTYPE: unknown dtype";
         case GSPN_ERR_ALIGN: return "GSPN_ERR_ALIGN: a base pointer is not 16-byte aligned";
-        case GSPN_ERR_ALIAS: return "GSPN_ERR_ALIAS: y overlaps an input";
+        case GSPN_ERR_ALIAS: return "GSPN_ERR_ALIAS: an output overlaps an input or another output";
         case GSPN_ERR_HIP: return "GSPN_ERR_HIP: a HIP call failed (see gspn_last_error)";
         case GSPN_ERR_PATH: return "GSPN_ERR_PATH: unknown path, or the path cannot run this shape";
         default: return "unknown GSPN status";
@@ -129,6 +129,58 @@ int gspn_scan_fwd(const void* x, const void* w_raw, const void* lam, const void*
                   int32_t ch_per_weight, int32_t dtype, hipStream_t stream) {
     return gspn_scan_fwd_path(x, w_raw, lam, u, y, B, C, H, W, dirs, groups, ch_per_weight, dtype,
                               GSPN_PATH_AUTO, stream);
+}
+
+int gspn_bwd_supported(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
+                       int32_t ch_per_weight, int32_t dtype) {
+    const int rc = check_sizes(B, C, H, W, dirs, groups, ch_per_weight, dtype);
+    if (rc) return rc;
+    return gspn::lines_supported((int)H, (int)W) ? GSPN_OK : GSPN_ERR_PATH;
+}
+
+int gspn_scan_bwd(const void* x, const void* w_raw, const void* lam, const void* u, const void* gy,
+                  void* gx, void* gw_raw, void* glam, void* gu, int64_t B, int64_t C, int64_t H,
+                  int64_t W, uint32_t dirs, int32_t groups, int32_t ch_per_weight, int32_t dtype,
+                  hipStream_t stream) {
+    g_last_error[0] = '\0';
+    int rc = check_sizes(B, C, H, W, dirs, groups, ch_per_weight, dtype);
+    if (rc) return rc;
+    if (!x || !w_raw || !lam || !u || !gy || !gx || !gw_raw || !glam || !gu) return GSPN_ERR_NULL;
+    const void* ptrs[9] = {x, w_raw, lam, u, gy, gx, gw_raw, glam, gu};
+    for (const void* q : ptrs)
+        if ((uintptr_t)q & 15u) return GSPN_ERR_ALIGN;
+    const size_t es = dtype == GSPN_BF16 ? 2 : 4;
+    const size_t nbytes = (size_t)B * C * H * W * es;
+    const size_t wbytes = (size_t)popcount4(dirs) * B * (C / ch_per_weight) * 3 * H * W * es;
+    // every output is disjoint from every input and from the other outputs
+    const void* outs[4] = {gx, gw_raw, glam, gu};
+    const size_t out_bytes[4] = {nbytes, wbytes, nbytes, nbytes};
+    const void* ins[5] = {x, w_raw, lam, u, gy};
+    const size_t in_bytes[5] = {nbytes, wbytes, nbytes, nbytes, nbytes};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return GSPN_ERR_ALIAS;
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return GSPN_ERR_ALIAS;
+    }
+    if (!gspn::lines_supported((int)H, (int)W)) {
+        set_error_text("the backward runs on the line kernels: H, W <= 512 and multiples of K");
+        return GSPN_ERR_PATH;
+    }
+
+    gspn::GradArgs g;
+    g.fwd.x = x; g.fwd.w = w_raw; g.fwd.lam = lam; g.fwd.u = u; g.fwd.y = nullptr;
+    g.fwd.B = (int)B; g.fwd.C = (int)C; g.fwd.H = (int)H; g.fwd.W = (int)W;
+    g.fwd.dirs = dirs; g.fwd.groups = groups; g.fwd.cpw = ch_per_weight; g.fwd.bf16 = dtype == GSPN_BF16;
+    g.gy = gy; g.gx = gx; g.gw = gw_raw; g.glam = glam; g.gu = gu;
+    void* work = nullptr;
+    hipError_t e = hipMallocAsync(&work, gspn::lines_bwd_workspace_bytes(g), stream);
+    if (e != hipSuccess) { set_error("hipMallocAsync(workspace)", e); return GSPN_ERR_HIP; }
+    e = gspn::launch_lines_bwd(g, work, stream);
+    const hipError_t ef = hipFreeAsync(work, stream);
+    if (e != hipSuccess) { set_error("backward kernel launch", e); return GSPN_ERR_HIP; }
+    if (ef != hipSuccess) { set_error("hipFreeAsync(workspace)", ef); return GSPN_ERR_HIP; }
+    return GSPN_OK;
 }
 
 }  // extern "C"

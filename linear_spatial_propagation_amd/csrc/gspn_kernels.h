@@ -43,6 +43,19 @@ bool lines_supported(int H, int W);
 size_t lines_workspace_bytes(const ScanArgs& a);
 hipError_t launch_lines(const ScanArgs& a, void* workspace, hipStream_t stream);
 
+// Backward on the line kernels (same shapes as lines_supported): the
+// forward's ScanArgs (y unused) plus dL/dy and the four gradients.
+struct GradArgs {
+    ScanArgs fwd;
+    const void* gy;
+    void* gx;
+    void* gw;      // dL/d raw taps, layout of w
+    void* glam;
+    void* gu;
+};
+size_t lines_bwd_workspace_bytes(const GradArgs& g);
+hipError_t launch_lines_bwd(const GradArgs& g, void* workspace, hipStream_t stream);
+
 // Per-line fallback: any H, W <= 4096.  `planes` is an fp32 workspace of
 // popcount(dirs) * B*C*H*W floats.
 hipError_t launch_general(const ScanArgs& a, float* planes, hipStream_t stream);

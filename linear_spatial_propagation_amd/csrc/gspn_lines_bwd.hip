@@ -1,0 +1,464 @@
+// gspn_lines_bwd.hip -- backward of the GSPN line scan (sides up to 512).
+//
+// The gradients are the exact vector-Jacobian product of the forward
+// operator ("Parallel Sequence Modeling via Generalized Spatial Propagation
+// Network", CVPR 2025 paper notes, "Key design 1-3"; the GSPN-2 author
+// response notes that the backward runs with the same speed-up as the
+// forward, "How Channel-shared Weight Mitigates the Concurrency
+// Bottleneck?").  With S = sum_dir h_dir and G = sum_dir g_dir:
+//   gu = gy * S;   gx = lam * G;   glam = x * G
+//   g_i = gy*u (at line i) + w_{i+1}^T g_{i+1}   (adjoint, last line first;
+//         the second term is cut at the first line of a group)
+//   dL/dw_t[i][p] = sum over the channels of a weight set of
+//                   g_i[p] * h_{i-1}[p+t-1]
+//   dL/da_t = w_t (1 - sigmoid(a_t)) (dL/dw_t - sum_v dL/dw_v w_v)
+//         (sigmoid-then-normalise; 0 on the taps the forward never reads).
+//
+// Launches, in order, on the caller's stream:
+//  1. transpose_kernel: x, lambda, gy, u and the LR/RL raw taps to [W][H];
+//  2. line_scan_kernel: the forward again, h of every direction into fp32
+//     planes;
+//  3. merge_kernel: gu = gy * sum of the planes;
+//  4. adjoint_scan_kernel: one wave per (direction, b, weight set); the CH
+//     channels of a chunk of the set run in lockstep, so each pixel's taps
+//     are normalised once for all of them and their tap gradients are summed
+//     in registers.  g overwrites h in the planes (line i's slot is free once
+//     line i+1 has used h_i); dL/da goes to an fp32 workspace, line-major.
+//     Sets with more channels than one chunk take one launch per chunk, the
+//     later ones adding to the workspace;
+//  5. merge_kernel: gx = lam * G, glam = x * G;
+//  6. the tap gradients to the caller's layout and dtype (transposed back for
+//     LR / RL).
+#include "gspn_lines.h"
+
+namespace gspn {
+namespace {
+
+struct AdjointParams {
+    const void* gy;     // [B][C][H][W]
+    const void* u;
+    const void* gyT;    // [B][C][W][H] (when LR or RL is enabled)
+    const void* uT;
+    const void* w;      // raw taps [nd][B][Cw][3][H][W]
+    const void* wT;     // [ncol][B][Cw][3][W][H]
+    float* planes;      // [nd][B][C][n][m]: h on entry, the adjoint g on exit
+    float* ga;          // [nd][B][Cw][3][n][m]: dL/d raw taps, line-major
+    float* sink;        // absorbs the stores of idle lanes and finished steps
+    int B, C, H, W, Cw, cpw, groups, nd;
+    int chunk;          // this launch runs channels chunk*CH .. chunk*CH+CH-1 of every set
+    int dir_of_slot[4];
+    int col_index[4];
+};
+
+template <int K>
+__device__ __forceinline__ void load_f32(float (&dst)[K], const float* p) {
+    if constexpr (K == 1) {
+        dst[0] = p[0];
+    } else if constexpr (K == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(p);
+        dst[0] = v.x; dst[1] = v.y;
+    } else {
+#pragma unroll
+        for (int e = 0; e < K; e += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(p + e);
+            dst[e] = v.x; dst[e + 1] = v.y; dst[e + 2] = v.z; dst[e + 3] = v.w;
+        }
+    }
+}
+
+template <int K>
+__device__ __forceinline__ void store_f32(float* p, const float (&v)[K]) {
+    if constexpr (K == 1) {
+        p[0] = v[0];
+    } else if constexpr (K == 2) {
+        *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < K; e += 4) *reinterpret_cast<float4*>(p + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+    }
+}
+
+// Everything one reverse step reads, for one lane.
+template <typename T, int K, int CH, bool ACC>
+struct AdjointStep {
+    LineVec<T, K> a[3];          // raw taps of line i
+    LineVec<T, K> gy[CH], u[CH]; // at line i
+    float hp[CH][K];             // h_{i-1}
+    float gp[ACC ? 3 : 1][K];    // earlier chunks' dL/da at line i (ACC only)
+};
+
+template <typename T, int K, int CH, bool ACC>
+__global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
+    const int lane = threadIdx.x & 63;
+    const int unit = blockIdx.x * 4 + uniform(threadIdx.x >> 6);   // (slot, b, k), k fastest
+    const int B = prm.B, C = prm.C, Cw = prm.Cw;
+    if (unit >= prm.nd * B * Cw) return;   // whole wave
+    const int k = unit % Cw;
+    const int b = (unit / Cw) % B;
+    const int slot = unit / (Cw * B);
+    const int d = prm.dir_of_slot[slot];
+    const bool is_row = d < 2;
+    const bool asc = d == 0 || d == 2;
+    const int H = prm.H, W = prm.W;
+    const size_t HW = (size_t)H * W;
+    const int n = is_row ? H : W;   // lines
+    const int m = is_row ? W : H;   // positions per line
+    const int L = n / prm.groups;
+    const int cbase = k * prm.cpw + prm.chunk * CH;
+
+    // every tensor is read as [n][m], line-major; channel ch at + ch * HW
+    const T* gys = static_cast<const T*>(is_row ? prm.gy : prm.gyT) + ((size_t)b * C + cbase) * HW;
+    const T* us = static_cast<const T*>(is_row ? prm.u : prm.uT) + ((size_t)b * C + cbase) * HW;
+    const T* ws = is_row
+        ? static_cast<const T*>(prm.w) + ((size_t)(slot * B + b) * Cw + k) * 3 * HW
+        : static_cast<const T*>(prm.wT) + ((size_t)(prm.col_index[slot] * B + b) * Cw + k) * 3 * HW;
+    float* pl = prm.planes + ((size_t)slot * B * C + (size_t)b * C + cbase) * HW;
+    float* gas = prm.ga + ((size_t)(slot * B + b) * Cw + k) * 3 * HW;
+
+    // lane's positions p0 .. p0+K-1; lanes past the line read a clamped
+    // vector and hold g = 0 (masks the compiler cannot see through keep the
+    // code branch-free, as in the forward scan)
+    const int p0 = K * lane;
+    const bool lane_on = p0 < m;
+    const int pc = lane_on ? p0 : m - K;
+    auto opaque = [](bool on) {
+        uint32_t v = on ? 0xffffffffu : 0u;
+        asm volatile("" : "+v"(v));
+        return v;
+    };
+    const uint32_t ml = opaque(lane_on);
+    const uint32_t m0 = opaque(lane_on && p0 >= 1);
+    const uint32_t m2 = opaque(lane_on && p0 + K < m);
+    const float f0 = lane_on && p0 >= 1 ? 1.0f : 0.0f;
+    const float f2 = lane_on && p0 + K < m ? 1.0f : 0.0f;
+    const float fl = lane_on ? 1.0f : 0.0f;
+    auto masked = [](float v, uint32_t msk) { return __uint_as_float(__float_as_uint(v) & msk); };
+
+    using Step = AdjointStep<T, K, CH, ACC>;
+    auto load_step = [&](Step& q, int i) {   // 0 <= i < n
+        const int j = asc ? i : n - 1 - i;
+        const size_t o = (size_t)j * m + pc;
+        q.a[0].load(ws + o);
+        q.a[1].load(ws + HW + o);
+        q.a[2].load(ws + 2 * HW + o);
+#pragma unroll
+        for (int ch = 0; ch < CH; ++ch) {
+            q.gy[ch].load(gys + ch * HW + o);
+            q.u[ch].load(us + ch * HW + o);
+        }
+        const int ip = i > 0 ? i - 1 : 0;
+        const size_t op = (size_t)(asc ? ip : n - 1 - ip) * m + pc;
+#pragma unroll
+        for (int ch = 0; ch < CH; ++ch) load_f32<K>(q.hp[ch], pl + ch * HW + op);
+        if constexpr (ACC) {
+#pragma unroll
+            for (int t = 0; t < 3; ++t) load_f32<K>(q.gp[t], gas + t * HW + o);
+        }
+    };
+
+    Step buf[kDepth];
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) load_step(buf[s], max(n - 1 - s, 0));
+
+    float carry[CH][K];   // w_{i+1}^T g_{i+1}
+#pragma unroll
+    for (int ch = 0; ch < CH; ++ch)
+#pragma unroll
+        for (int e = 0; e < K; ++e) carry[ch][e] = 0.0f;
+
+    for (int s0 = 0; s0 < n; s0 += kDepth) {
+#pragma unroll
+        for (int s = 0; s < kDepth; ++s) {
+            const int i = n - 1 - (s0 + s);            // < 0: past the last step
+            const Step& q = buf[s];
+            const bool live = i >= 0;
+            const bool coupled = live && i % L != 0;   // line i reads line i-1 (uniform)
+            const int j = asc ? i : n - 1 - i;
+            const bool put = live && lane_on;
+
+            float g[CH][K];
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch) {
+#pragma unroll
+                for (int e = 0; e < K; ++e)
+                    g[ch][e] = fmaf(masked(q.gy[ch].get(e), ml), masked(q.u[ch].get(e), ml), carry[ch][e]);
+                store_f32<K>(put ? pl + ch * HW + (size_t)j * m + p0 : prm.sink + K * lane, g[ch]);
+            }
+
+            float ga[3][K];
+            if (coupled) {
+                // tap gradients summed over the chunk's channels
+                float dw[3][K];
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+#pragma unroll
+                    for (int e = 0; e < K; ++e) dw[t][e] = 0.0f;
+#pragma unroll
+                for (int ch = 0; ch < CH; ++ch) {
+                    const float left = from_left(q.hp[ch][K - 1]);
+                    const float right = from_right(q.hp[ch][0]);
+#pragma unroll
+                    for (int e = 0; e < K; ++e) {
+                        const float hl = e == 0 ? left : q.hp[ch][e - 1];
+                        const float hr = e == K - 1 ? right : q.hp[ch][e + 1];
+                        dw[0][e] = fmaf(g[ch][e], hl, dw[0][e]);
+                        dw[1][e] = fmaf(g[ch][e], q.hp[ch][e], dw[1][e]);
+                        dw[2][e] = fmaf(g[ch][e], hr, dw[2][e]);
+                    }
+                }
+                // weights of line i and 1 - sigmoid of its taps
+                float a0[K], a1[K], a2[K], w0[K], w1[K], w2[K], o0[K], o1[K], o2[K];
+                float amin = 0.0f;
+#pragma unroll
+                for (int e = 0; e < K; ++e) {
+                    a0[e] = masked(q.a[0].get(e), e == 0 ? m0 : ml);   // missing taps -> 0
+                    a1[e] = masked(q.a[1].get(e), ml);
+                    a2[e] = masked(q.a[2].get(e), e == K - 1 ? m2 : ml);
+                    amin = fminf(amin, fminf(fminf(a0[e], a1[e]), a2[e]));
+                }
+                const float kNegLog2e = -1.44269504088896340736f;
+                if (__builtin_amdgcn_ballot_w64(amin < -40.0f) == 0) {
+                    // exp(-a) <= e^40: no overflow; 1 - sigmoid(a) = e * sigmoid(a)
+#pragma unroll
+                    for (int e = 0; e < K; ++e) {
+                        const float e0 = fast_exp2(a0[e] * kNegLog2e);
+                        const float e1 = fast_exp2(a1[e] * kNegLog2e);
+                        const float e2 = fast_exp2(a2[e] * kNegLog2e);
+                        const float s0 = fast_rcp(1.0f + e0) * (e == 0 ? f0 : fl);
+                        const float s1 = fast_rcp(1.0f + e1);
+                        const float s2 = fast_rcp(1.0f + e2) * (e == K - 1 ? f2 : fl);
+                        const float inv = fast_rcp(s0 + s1 + s2);
+                        w0[e] = s0 * inv; w1[e] = s1 * inv; w2[e] = s2 * inv;
+                        o0[e] = e0 * s0; o1[e] = e1 * s1; o2[e] = e2 * s2;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < K; ++e) {
+                        const bool h0 = lane_on && p0 + e >= 1, h2 = lane_on && p0 + e + 1 < m;
+                        const Taps tp = normalise_taps(a0[e], a1[e], a2[e], h0, h2);
+                        w0[e] = tp.w0; w1[e] = tp.w1; w2[e] = tp.w2;
+                        const float av[3] = {a0[e], a1[e], a2[e]};
+                        float om[3];
+#pragma unroll
+                        for (int t = 0; t < 3; ++t) {
+                            const float ex = fast_exp2(av[t] * kNegLog2e);   // may be inf
+                            const float sg = fast_rcp(1.0f + ex);
+                            om[t] = av[t] >= 0.0f ? ex * sg : 1.0f - sg;
+                        }
+                        o0[e] = om[0]; o1[e] = om[1]; o2[e] = om[2];
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < K; ++e) {
+                    const float dot = fmaf(dw[0][e], w0[e], fmaf(dw[1][e], w1[e], dw[2][e] * w2[e]));
+                    ga[0][e] = w0[e] * o0[e] * (dw[0][e] - dot);
+                    ga[1][e] = w1[e] * o1[e] * (dw[1][e] - dot);
+                    ga[2][e] = w2[e] * o2[e] * (dw[2][e] - dot);
+                }
+                // carry into line i-1: (w_i^T g_i)[p] = w1 g[p] + w0[p+1] g[p+1]
+                // + w2[p-1] g[p-1], with w1 = 1 - w0 - w2
+#pragma unroll
+                for (int ch = 0; ch < CH; ++ch) {
+                    float c0[K], c2[K];
+#pragma unroll
+                    for (int e = 0; e < K; ++e) {
+                        c0[e] = w0[e] * g[ch][e];
+                        c2[e] = w2[e] * g[ch][e];
+                    }
+                    const float r0 = from_right(c0[0]);
+                    const float l2 = from_left(c2[K - 1]);
+#pragma unroll
+                    for (int e = 0; e < K; ++e)
+                        carry[ch][e] = (g[ch][e] - c0[e] - c2[e]) + (e == K - 1 ? r0 : c0[e + 1]) +
+                                       (e == 0 ? l2 : c2[e - 1]);
+                }
+            } else {
+                // first line of a group: its taps are unused, nothing flows on
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+#pragma unroll
+                    for (int e = 0; e < K; ++e) ga[t][e] = 0.0f;
+#pragma unroll
+                for (int ch = 0; ch < CH; ++ch)
+#pragma unroll
+                    for (int e = 0; e < K; ++e) carry[ch][e] = 0.0f;
+            }
+            if constexpr (ACC) {
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+#pragma unroll
+                    for (int e = 0; e < K; ++e) ga[t][e] += q.gp[t][e];
+            }
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+                store_f32<K>(put ? gas + t * HW + (size_t)j * m + p0 : prm.sink + K * lane, ga[t]);
+            // refill the slot with the step kDepth ahead (clamped), after use
+            load_step(buf[s], max(i - kDepth, 0));
+        }
+    }
+}
+
+// fp32 -> storage dtype, 8 elements per thread when `vec` (16-byte aligned,
+// count % 8 == 0), else one.
+template <typename T>
+__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ src, T* __restrict__ dst, size_t count,
+                                                      int vec) {
+    const size_t tid = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (vec) {
+        const size_t e = tid * 8;
+        if (e >= count) return;
+        float f[8];
+        const float4 v0 = *reinterpret_cast<const float4*>(src + e);
+        const float4 v1 = *reinterpret_cast<const float4*>(src + e + 4);
+        f[0] = v0.x; f[1] = v0.y; f[2] = v0.z; f[3] = v0.w; f[4] = v1.x; f[5] = v1.y; f[6] = v1.z; f[7] = v1.w;
+        if constexpr (sizeof(T) == 2) {
+            store16_nt(dst + e, f);
+        } else {
+            const float a[4] = {f[0], f[1], f[2], f[3]}, c[4] = {f[4], f[5], f[6], f[7]};
+            store16_nt(dst + e, a);
+            store16_nt(dst + e + 4, c);
+        }
+        return;
+    }
+    if (tid < count) dst[tid] = from_f32(src[tid], (T*)nullptr);
+}
+
+template <typename T>
+void launch_adjoint(const AdjointParams& p, int K, int CH, bool acc, hipStream_t stream) {
+    const long units = (long)p.nd * p.B * p.Cw;
+    const dim3 grid((unsigned)((units + 3) / 4)), block(256);
+#define GSPN_ADJ(KK, CC)                                                                                      \
+    if (K == KK && CH == CC) {                                                                                \
+        if (acc) hipLaunchKernelGGL((adjoint_scan_kernel<T, KK, CC, true>), grid, block, 0, stream, p);       \
+        else hipLaunchKernelGGL((adjoint_scan_kernel<T, KK, CC, false>), grid, block, 0, stream, p);          \
+        return;                                                                                               \
+    }
+    GSPN_ADJ(1, 1) GSPN_ADJ(1, 2) GSPN_ADJ(1, 4) GSPN_ADJ(1, 8)
+    GSPN_ADJ(2, 1) GSPN_ADJ(2, 2) GSPN_ADJ(2, 4)
+    GSPN_ADJ(4, 1) GSPN_ADJ(4, 2)
+    GSPN_ADJ(8, 1)
+#undef GSPN_ADJ
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+    size_t planes, sink, xT, lamT, gyT, uT, wT, ga, total;
+};
+
+BwdLayout bwd_layout(const GradArgs& g) {
+    const ScanArgs& a = g.fwd;
+    const size_t E = (size_t)a.B * a.C * a.H * a.W;
+    const size_t es = a.bf16 ? 2 : 4;
+    int dos[4], ci[4], ncol = 0;
+    const int nd = enabled_slots(a.dirs, dos, ci, &ncol);
+    const size_t Ew = (size_t)a.B * (a.C / a.cpw) * 3 * a.H * a.W;
+    BwdLayout l;
+    size_t o = 0;
+    l.planes = o; o += align256((size_t)nd * E * sizeof(float));
+    l.sink = o;   o += align256(kSinkBytes);
+    l.xT = l.lamT = l.gyT = l.uT = l.wT = 0;
+    if (ncol) {
+        l.xT = o;   o += align256(E * es);
+        l.lamT = o; o += align256(E * es);
+        l.gyT = o;  o += align256(E * es);
+        l.uT = o;   o += align256(E * es);
+        l.wT = o;   o += align256((size_t)ncol * Ew * es);
+    }
+    l.ga = o; o += align256((size_t)nd * Ew * sizeof(float));
+    l.total = o;
+    return l;
+}
+
+template <typename T>
+hipError_t launch_lines_bwd_t(const GradArgs& g, void* workspace, hipStream_t stream) {
+    const ScanArgs& a = g.fwd;
+    const int H = a.H, W = a.W;
+    const int Cw = a.C / a.cpw;
+    const BwdLayout l = bwd_layout(g);
+    char* base = static_cast<char*>(workspace);
+    float* planes = reinterpret_cast<float*>(base + l.planes);
+    float* sink = reinterpret_cast<float*>(base + l.sink);
+    T* xT = reinterpret_cast<T*>(base + l.xT);
+    T* lamT = reinterpret_cast<T*>(base + l.lamT);
+    T* gyT = reinterpret_cast<T*>(base + l.gyT);
+    T* uT = reinterpret_cast<T*>(base + l.uT);
+    T* wT = reinterpret_cast<T*>(base + l.wT);
+    float* ga = reinterpret_cast<float*>(base + l.ga);
+
+    LineParams p;
+    p.x = a.x; p.lam = a.lam; p.w = a.w;
+    p.xT = xT; p.lamT = lamT; p.wT = wT;
+    p.planes = planes;
+    p.sink = sink;
+    p.B = a.B; p.C = a.C; p.H = H; p.W = W; p.Cw = Cw; p.cpw = a.cpw; p.groups = a.groups;
+    int ncol = 0;
+    p.nd = enabled_slots(a.dirs, p.dir_of_slot, p.col_index, &ncol);
+    const size_t slices = (size_t)a.B * a.C;
+    const size_t wslab = (size_t)a.B * Cw * 3;          // [H][W] planes per slab
+    const size_t HW = (size_t)H * W;
+
+    // 1. column-major copies for LR / RL
+    if (ncol > 0) {
+        launch_transpose(static_cast<const T*>(a.x), xT, slices, H, W, stream);
+        launch_transpose(static_cast<const T*>(a.lam), lamT, slices, H, W, stream);
+        launch_transpose(static_cast<const T*>(g.gy), gyT, slices, H, W, stream);
+        launch_transpose(static_cast<const T*>(a.u), uT, slices, H, W, stream);
+        for (int s = 0; s < p.nd; ++s) {
+            if (p.dir_of_slot[s] < 2) continue;
+            launch_transpose(static_cast<const T*>(a.w) + (size_t)s * wslab * HW,
+                             wT + (size_t)p.col_index[s] * wslab * HW, wslab, H, W, stream);
+        }
+    }
+    // 2. forward states
+    launch_line_scan<T>(p, stream);
+    // 3. gu = gy * sum_dir h_dir
+    MergeParams q;
+    q.planes = planes;
+    q.B = a.B; q.C = a.C; q.H = H; q.W = W; q.nd = p.nd;
+    for (int s = 0; s < 4; ++s) q.dir_of_slot[s] = p.dir_of_slot[s];
+    q.in[0] = g.gy; q.out[0] = g.gu; q.in[1] = nullptr; q.out[1] = nullptr;
+    launch_merge<T, 1>(q, stream);
+    // 4. adjoint scans, one launch per chunk of channels
+    AdjointParams r;
+    r.gy = g.gy; r.u = a.u; r.gyT = gyT; r.uT = uT; r.w = a.w; r.wT = wT;
+    r.planes = planes; r.ga = ga; r.sink = sink;
+    r.B = a.B; r.C = a.C; r.H = H; r.W = W; r.Cw = Cw; r.cpw = a.cpw; r.groups = a.groups; r.nd = p.nd;
+    for (int s = 0; s < 4; ++s) { r.dir_of_slot[s] = p.dir_of_slot[s]; r.col_index[s] = p.col_index[s]; }
+    const int K = lines_positions_per_lane(H, W);
+    int CH = 8 / K;
+    while (a.cpw % CH) CH /= 2;
+    for (int c = 0; c < a.cpw / CH; ++c) {
+        r.chunk = c;
+        launch_adjoint<T>(r, K, CH, c > 0, stream);
+    }
+    // 5. gx = lam * G, glam = x * G
+    q.in[0] = a.lam; q.out[0] = g.gx; q.in[1] = a.x; q.out[1] = g.glam;
+    launch_merge<T, 2>(q, stream);
+    // 6. tap gradients in the caller's layout and dtype
+    const size_t slab = wslab * HW;
+    for (int s = 0; s < p.nd; ++s) {
+        const float* src = ga + (size_t)s * slab;
+        T* dst = static_cast<T*>(g.gw) + (size_t)s * slab;
+        if (p.dir_of_slot[s] >= 2) {
+            launch_transpose(src, dst, wslab, W, H, stream);   // [W][H] -> [H][W]
+        } else {
+            const int vec = slab % 8 == 0 && ((uintptr_t)dst & 15u) == 0;
+            const size_t threads = vec ? slab / 8 : slab;
+            hipLaunchKernelGGL(convert_kernel<T>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                               src, dst, slab, vec);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t lines_bwd_workspace_bytes(const GradArgs& g) { return bwd_layout(g).total; }
+
+hipError_t launch_lines_bwd(const GradArgs& g, void* workspace, hipStream_t stream) {
+    return g.fwd.bf16 ? launch_lines_bwd_t<uint16_t>(g, workspace, stream)
+                      : launch_lines_bwd_t<float>(g, workspace, stream);
+}
+
+}  // namespace gspn

@@ -13,8 +13,9 @@ Streams are per slice so that any slice can be regenerated alone:
   x, lam, u of slice (b, c)      <- default_rng([seed, 0, b, c]), drawn in
                                     the order x, lam, u;
   w_raw of (direction bit d, b, k) <- default_rng([seed, 1, d, b, k]).
+  the upstream gradient gy of slice (b, c) <- default_rng([seed, 2, b, c]).
 Value distributions: x ~ N(0, 1), raw taps ~ N(0, 1), lam ~ U(0, 1),
-u ~ U(0, 1) (or u = 1).  Values are drawn in float32 and, for bf16
+u ~ U(0, 1) (or u = 1), gy ~ N(0, 1).  Values are drawn in float32 and, for bf16
 workloads, rounded to bf16 with round-to-nearest-even.
 """
 from __future__ import annotations
@@ -115,6 +116,27 @@ def slice_w(seed: int, d: int, b: int, k: int, H: int, W: int) -> np.ndarray:
     """float32 raw taps [3][H][W] of direction bit ``d`` for weight set (b, k)."""
     rng = np.random.default_rng([seed, 1, d, b, k])
     return rng.standard_normal(3 * H * W, dtype=np.float32).reshape(3, H, W)
+
+
+def slice_gy(seed: int, b: int, c: int, H: int, W: int) -> np.ndarray:
+    """float32 upstream gradient dL/dy [H][W] of slice (b, c)."""
+    rng = np.random.default_rng([seed, 2, b, c])
+    return rng.standard_normal(H * W, dtype=np.float32).reshape(H, W)
+
+
+def make_gy(wl: "Workload", seed: int) -> np.ndarray:
+    """Storage-dtype dL/dy [B][C][H][W] for a workload, slice by slice."""
+    st = np.uint16 if wl.dtype == "bf16" else np.float32
+    gy = np.empty((wl.B, wl.C, wl.H, wl.W), st)
+    for b in range(wl.B):
+        for c in range(wl.C):
+            gy[b, c] = _store(slice_gy(seed, b, c, wl.H, wl.W), wl.dtype)
+    return gy
+
+
+def gy_f64(gy_store: np.ndarray, dtype: str) -> np.ndarray:
+    """The exact device values of a stored gradient, widened to float64."""
+    return bf16_bits_to_f32(gy_store).astype(np.float64) if dtype == "bf16" else gy_store.astype(np.float64)
 
 
 def make_workload(B: int, C: int, H: int, W: int, *, dirs: int = 15, groups: int = 1,

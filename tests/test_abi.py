@@ -102,3 +102,39 @@ def test_check_raises_with_status(lib):
     with pytest.raises(gspn.GspnError) as ei:
         _lib.check(-4)
     assert ei.value.status == -4
+
+
+def call_bwd(**kw):
+    names = ("x", "w", "lam", "u", "gy", "gx", "gw", "glam", "gu")
+    args = {nm: FAKE + (i << 32) for i, nm in enumerate(names)}
+    args.update(B=2, C=8, H=16, W=16, dirs=15, groups=1, ch_per_weight=1, dtype=1)
+    args.update(kw)
+    return _lib.scan_bwd_ptr(*(args[nm] for nm in names), args["B"], args["C"], args["H"], args["W"],
+                             dirs=args["dirs"], groups=args["groups"],
+                             ch_per_weight=args["ch_per_weight"], dtype=args["dtype"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(W=4097), -2), (dict(dirs=0), -3), (dict(groups=3), -4),
+    (dict(ch_per_weight=3), -5), (dict(dtype=2), -6),
+    (dict(x=0), -1), (dict(gy=0), -1), (dict(gx=0), -1), (dict(gw=0), -1), (dict(glam=0), -1),
+    (dict(gu=0), -1),
+    (dict(gy=FAKE + 8), -7), (dict(gw=FAKE + (6 << 32) + 4), -7),
+    (dict(gx=FAKE), -8),                          # output on an input
+    (dict(gu=FAKE + (4 << 32) + 512), -8),        # output inside gy
+    (dict(glam=FAKE + (5 << 32) + 16), -8),       # two outputs overlap
+    (dict(gw=FAKE + (1 << 32)), -8),              # tap gradients on the taps
+    (dict(H=1000, W=16), -10), (dict(H=130, W=16), -10), (dict(H=600, W=600), -10),
+])
+def test_bwd_invalid_arguments_rejected_on_host(lib, kw, code):
+    assert call_bwd(**kw) == code
+
+
+def test_bwd_supported(lib):
+    assert _lib.bwd_supported(32, 128, 64, 64, ch_per_weight=8) == 0
+    assert _lib.bwd_supported(64, 96, 56, 56) == 0
+    assert _lib.bwd_supported(8, 256, 128, 128, groups=8) == 0
+    assert _lib.bwd_supported(1, 320, 512, 512) == 0
+    assert _lib.bwd_supported(1, 8, 130, 64) == -10     # 130 is not a multiple of K = 4
+    assert _lib.bwd_supported(1, 8, 513, 64) == -10
+    assert _lib.bwd_supported(1, 8, 32, 32, groups=5) == -4
