@@ -178,8 +178,10 @@ int gspn_select_path(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, 
  * channels in a fixed order (deterministic).
  * Shapes: H, W <= 512 and both multiples of K (as for the forward's line
  * kernels), else GSPN_ERR_PATH; gspn_bwd_supported tells in advance.
- * Workspace, taken stream-ordered on `stream` (hipMallocAsync/hipFreeAsync),
- * each part rounded up to 256 bytes:
+ * H <= 64 and W <= 64 run one fused kernel (one workgroup per weight set,
+ * all states in LDS) and allocate nothing.  Larger shapes run the line
+ * kernels with a workspace taken stream-ordered on `stream`
+ * (hipMallocAsync/hipFreeAsync), each part rounded up to 256 bytes:
  *   popcount(dirs) * B*C*H*W * 4 (fp32 states, then adjoints) + 2 KiB
  *   + popcount(dirs) * B*(C/cpw)*3*H*W * 4 (fp32 tap gradients)
  *   + if LR or RL is enabled: (4 * B*C*H*W + ncol * B*(C/cpw)*3*H*W) * s
@@ -190,6 +192,14 @@ int gspn_scan_bwd(const void *x, const void *w_raw, const void *lam, const void 
                   void *gx, void *gw_raw, void *glam, void *gu, int64_t B, int64_t C, int64_t H,
                   int64_t W, uint32_t dirs, int32_t groups, int32_t ch_per_weight, int32_t dtype,
                   hipStream_t stream);
+
+/* Same operation on a chosen kernel path (GSPN_PATH_FUSED: H, W <= 64;
+ * GSPN_PATH_GENERAL: the line kernels); used to cross-check the paths.
+ * GSPN_ERR_PATH if the path cannot run the shape. */
+int gspn_scan_bwd_path(const void *x, const void *w_raw, const void *lam, const void *u, const void *gy,
+                       void *gx, void *gw_raw, void *glam, void *gu, int64_t B, int64_t C, int64_t H,
+                       int64_t W, uint32_t dirs, int32_t groups, int32_t ch_per_weight, int32_t dtype,
+                       int32_t path, hipStream_t stream);
 
 /* GSPN_OK if gspn_scan_bwd can run these sizes, GSPN_ERR_PATH if the shape is
  * outside its kernels, or another negative code for invalid sizes. */

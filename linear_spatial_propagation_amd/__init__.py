@@ -60,7 +60,7 @@ def _check_inputs(tensors, dirs, ch_per_weight):
 
 
 def scan_bwd(x, w_raw, lam, u, gy, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1,
-             out=None):
+             out=None, path: int = PATH_AUTO):
     """Backward GSPN scan on the current HIP stream.
 
     Returns (gx, gw_raw, glam, gu), the gradients of a loss whose gradient
@@ -84,7 +84,8 @@ def scan_bwd(x, w_raw, lam, u, gy, *, dirs: int = DIR_ALL, groups: int = 1, ch_p
         rc = _lib.scan_bwd_ptr(x.data_ptr(), w_raw.data_ptr(), lam.data_ptr(), u.data_ptr(),
                                gy.data_ptr(), gx.data_ptr(), gw.data_ptr(), glam.data_ptr(),
                                gu.data_ptr(), B, C, H, W, dirs=dirs, groups=groups,
-                               ch_per_weight=ch_per_weight, dtype=_dtype_code(x), stream=stream)
+                               ch_per_weight=ch_per_weight, dtype=_dtype_code(x), path=path,
+                               stream=stream)
     _lib.check(rc)
     return gx, gw, glam, gu
 

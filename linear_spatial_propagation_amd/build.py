@@ -16,7 +16,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgspn.so")
-SOURCES = ["gspn_api.hip", "gspn_fused.hip", "gspn_lines.hip", "gspn_lines_bwd.hip", "gspn_general.hip"]
+SOURCES = ["gspn_api.hip", "gspn_fused.hip", "gspn_lines.hip", "gspn_lines_bwd.hip", "gspn_fused_bwd.hip", "gspn_general.hip"]
 ARCH = "gfx950"
 
 

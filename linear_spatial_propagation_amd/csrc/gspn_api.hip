@@ -142,6 +142,14 @@ int gspn_scan_bwd(const void* x, const void* w_raw, const void* lam, const void*
                   void* gx, void* gw_raw, void* glam, void* gu, int64_t B, int64_t C, int64_t H,
                   int64_t W, uint32_t dirs, int32_t groups, int32_t ch_per_weight, int32_t dtype,
                   hipStream_t stream) {
+    return gspn_scan_bwd_path(x, w_raw, lam, u, gy, gx, gw_raw, glam, gu, B, C, H, W, dirs, groups,
+                              ch_per_weight, dtype, GSPN_PATH_AUTO, stream);
+}
+
+int gspn_scan_bwd_path(const void* x, const void* w_raw, const void* lam, const void* u, const void* gy,
+                       void* gx, void* gw_raw, void* glam, void* gu, int64_t B, int64_t C, int64_t H,
+                       int64_t W, uint32_t dirs, int32_t groups, int32_t ch_per_weight, int32_t dtype,
+                       int32_t path, hipStream_t stream) {
     g_last_error[0] = '\0';
     int rc = check_sizes(B, C, H, W, dirs, groups, ch_per_weight, dtype);
     if (rc) return rc;
@@ -163,7 +171,10 @@ int gspn_scan_bwd(const void* x, const void* w_raw, const void* lam, const void*
         for (int j = 0; j < i; ++j)
             if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return GSPN_ERR_ALIAS;
     }
-    if (!gspn::lines_supported((int)H, (int)W)) {
+    if (path == GSPN_PATH_AUTO) path = auto_path(H, W);
+    if (path != GSPN_PATH_FUSED && path != GSPN_PATH_GENERAL) return GSPN_ERR_PATH;
+    if (path == GSPN_PATH_FUSED && auto_path(H, W) != GSPN_PATH_FUSED) return GSPN_ERR_PATH;
+    if (path == GSPN_PATH_GENERAL && !gspn::lines_supported((int)H, (int)W)) {
         set_error_text("the backward runs on the line kernels: H, W <= 512 and multiples of K");
         return GSPN_ERR_PATH;
     }
@@ -173,6 +184,11 @@ int gspn_scan_bwd(const void* x, const void* w_raw, const void* lam, const void*
     g.fwd.B = (int)B; g.fwd.C = (int)C; g.fwd.H = (int)H; g.fwd.W = (int)W;
     g.fwd.dirs = dirs; g.fwd.groups = groups; g.fwd.cpw = ch_per_weight; g.fwd.bf16 = dtype == GSPN_BF16;
     g.gy = gy; g.gx = gx; g.gw = gw_raw; g.glam = glam; g.gu = gu;
+    if (path == GSPN_PATH_FUSED) {
+        const hipError_t e = gspn::launch_fused_bwd(g, stream);
+        if (e != hipSuccess) { set_error("fused backward launch", e); return GSPN_ERR_HIP; }
+        return GSPN_OK;
+    }
     void* work = nullptr;
     hipError_t e = hipMallocAsync(&work, gspn::lines_bwd_workspace_bytes(g), stream);
     if (e != hipSuccess) { set_error("hipMallocAsync(workspace)", e); return GSPN_ERR_HIP; }

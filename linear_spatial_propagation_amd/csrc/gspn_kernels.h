@@ -53,6 +53,8 @@ struct GradArgs {
     void* glam;
     void* gu;
 };
+// Fused backward: H <= 64 and W <= 64, no workspace.
+hipError_t launch_fused_bwd(const GradArgs& g, hipStream_t stream);
 size_t lines_bwd_workspace_bytes(const GradArgs& g);
 hipError_t launch_lines_bwd(const GradArgs& g, void* workspace, hipStream_t stream);
 

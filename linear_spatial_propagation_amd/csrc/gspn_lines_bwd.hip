@@ -12,7 +12,8 @@
 //   dL/dw_t[i][p] = sum over the channels of a weight set of
 //                   g_i[p] * h_{i-1}[p+t-1]
 //   dL/da_t = w_t (1 - sigmoid(a_t)) (dL/dw_t - sum_v dL/dw_v w_v)
-//         (sigmoid-then-normalise; 0 on the taps the forward never reads).
+//         (sigmoid-then-normalise; 0 on the taps the forward never reads),
+//         evaluated from E0 = D0 - D1, E2 = D2 - D1 without cancellation.
 //
 // Launches, in order, on the caller's stream:
 //  1. transpose_kernel: x, lambda, gy, u and the LR/RL raw taps to [W][H];
@@ -187,12 +188,11 @@ __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
 
             float ga[3][K];
             if (coupled) {
-                // tap gradients summed over the chunk's channels
-                float dw[3][K];
+                // tap-gradient differences summed over the chunk's channels:
+                // E0 = sum g (h[p-1] - h[p]), E2 = sum g (h[p+1] - h[p])
+                float ed[2][K];
 #pragma unroll
-                for (int t = 0; t < 3; ++t)
-#pragma unroll
-                    for (int e = 0; e < K; ++e) dw[t][e] = 0.0f;
+                for (int e = 0; e < K; ++e) { ed[0][e] = 0.0f; ed[1][e] = 0.0f; }
 #pragma unroll
                 for (int ch = 0; ch < CH; ++ch) {
                     const float left = from_left(q.hp[ch][K - 1]);
@@ -201,9 +201,8 @@ __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
                     for (int e = 0; e < K; ++e) {
                         const float hl = e == 0 ? left : q.hp[ch][e - 1];
                         const float hr = e == K - 1 ? right : q.hp[ch][e + 1];
-                        dw[0][e] = fmaf(g[ch][e], hl, dw[0][e]);
-                        dw[1][e] = fmaf(g[ch][e], q.hp[ch][e], dw[1][e]);
-                        dw[2][e] = fmaf(g[ch][e], hr, dw[2][e]);
+                        ed[0][e] = fmaf(g[ch][e], hl - q.hp[ch][e], ed[0][e]);
+                        ed[1][e] = fmaf(g[ch][e], hr - q.hp[ch][e], ed[1][e]);
                     }
                 }
                 // weights of line i and 1 - sigmoid of its taps
@@ -248,12 +247,15 @@ __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
                         o0[e] = om[0]; o1[e] = om[1]; o2[e] = om[2];
                     }
                 }
+                // D_t - sum_v w_v D_v without cancellation (weights sum to 1):
+                //   t = 0: w1 E0 + w2 (E0 - E2); t = 1: -(w0 E0 + w2 E2);
+                //   t = 2: w1 E2 + w0 (E2 - E0)
 #pragma unroll
                 for (int e = 0; e < K; ++e) {
-                    const float dot = fmaf(dw[0][e], w0[e], fmaf(dw[1][e], w1[e], dw[2][e] * w2[e]));
-                    ga[0][e] = w0[e] * o0[e] * (dw[0][e] - dot);
-                    ga[1][e] = w1[e] * o1[e] * (dw[1][e] - dot);
-                    ga[2][e] = w2[e] * o2[e] * (dw[2][e] - dot);
+                    const float E0 = ed[0][e], E2 = ed[1][e];
+                    ga[0][e] = w0[e] * o0[e] * fmaf(w1[e], E0, w2[e] * (E0 - E2));
+                    ga[1][e] = -(w1[e] * o1[e] * fmaf(w0[e], E0, w2[e] * E2));
+                    ga[2][e] = w2[e] * o2[e] * fmaf(w1[e], E2, w0[e] * (E2 - E0));
                 }
                 // carry into line i-1: (w_i^T g_i)[p] = w1 g[p] + w0[p+1] g[p+1]
                 // + w2[p-1] g[p-1], with w1 = 1 - w0 - w2

@@ -107,11 +107,11 @@ def test_check_raises_with_status(lib):
 def call_bwd(**kw):
     names = ("x", "w", "lam", "u", "gy", "gx", "gw", "glam", "gu")
     args = {nm: FAKE + (i << 32) for i, nm in enumerate(names)}
-    args.update(B=2, C=8, H=16, W=16, dirs=15, groups=1, ch_per_weight=1, dtype=1)
+    args.update(B=2, C=8, H=16, W=16, dirs=15, groups=1, ch_per_weight=1, dtype=1, path=0)
     args.update(kw)
     return _lib.scan_bwd_ptr(*(args[nm] for nm in names), args["B"], args["C"], args["H"], args["W"],
                              dirs=args["dirs"], groups=args["groups"],
-                             ch_per_weight=args["ch_per_weight"], dtype=args["dtype"])
+                             ch_per_weight=args["ch_per_weight"], dtype=args["dtype"], path=args["path"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -125,6 +125,7 @@ def call_bwd(**kw):
     (dict(glam=FAKE + (5 << 32) + 16), -8),       # two outputs overlap
     (dict(gw=FAKE + (1 << 32)), -8),              # tap gradients on the taps
     (dict(H=1000, W=16), -10), (dict(H=130, W=16), -10), (dict(H=600, W=600), -10),
+    (dict(path=7), -10), (dict(path=1, W=65), -10), (dict(path=2, H=130), -10),
 ])
 def test_bwd_invalid_arguments_rejected_on_host(lib, kw, code):
     assert call_bwd(**kw) == code

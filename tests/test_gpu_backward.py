@@ -21,11 +21,14 @@ pytestmark = pytest.mark.gpu
 NAMES = ("gx", "gw", "glam", "gu")
 
 
-def run_bwd(wl, gy_store):
+PATHS = {"auto": 0, "fused": 1, "lines": 2}
+
+
+def run_bwd(wl, gy_store, path="auto"):
     import torch
     import linear_spatial_propagation_amd as gspn
     dev = [to_device(a, wl.dtype) for a in (wl.x_store, wl.w_store, wl.lam_store, wl.u_store, gy_store)]
-    out = gspn.scan_bwd(*dev, dirs=wl.dirs, groups=wl.groups, ch_per_weight=wl.cpw)
+    out = gspn.scan_bwd(*dev, dirs=wl.dirs, groups=wl.groups, ch_per_weight=wl.cpw, path=PATHS[path])
     torch.cuda.synchronize()
     return [from_device(t, wl.dtype) for t in out]
 
@@ -34,11 +37,11 @@ def errors(got, want, dtype):
     return {nm: parity_error(g, w, dtype) for nm, g, w in zip(NAMES, got, want)}
 
 
-def check(wl, seed):
+def check(wl, seed, path="auto"):
     say(f"case bwd B={wl.B} C={wl.C} H={wl.H} W={wl.W} dirs={wl.dirs} g={wl.groups} "
-        f"cpw={wl.cpw} {wl.dtype}")
+        f"cpw={wl.cpw} {wl.dtype} path={path}")
     gy = make_gy(wl, seed)
-    got = run_bwd(wl, gy)
+    got = run_bwd(wl, gy, path)
     want = oracle.scan_bwd(wl.x, wl.w, wl.lam, wl.u, gy_f64(gy, wl.dtype), dirs=wl.dirs,
                            groups=wl.groups, cpw=wl.cpw)
     errs = errors(got, want, wl.dtype)
@@ -85,8 +88,24 @@ def test_bwd_edge_shapes(case, dtype):
     check(make_workload(B, C, H, W, dirs=dirs, groups=g, cpw=cpw, dtype=dtype, seed=seed), seed + 100)
 
 
+# the line kernels on shapes that the fused kernel takes by default
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", [c for c in EDGE_BWD if max(c[2], c[3]) <= 64],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_bwd_edge_shapes_line_kernels(case, dtype):
+    B, C, H, W, dirs, g, cpw = case
+    seed = sum(case) + 7
+    check(make_workload(B, C, H, W, dirs=dirs, groups=g, cpw=cpw, dtype=dtype, seed=seed), seed + 100,
+          path="lines")
+
+
 def test_bwd_tiny_full():
     check(config_workload("tiny"), 11)
+
+
+@pytest.mark.parametrize("path", ["fused", "lines"])
+def test_bwd_cgspn1k_full(path):
+    check(config_workload("cgspn1k"), 1002, path=path)
 
 
 def sampled_sets(B, Cw, n, seed):
@@ -125,6 +144,17 @@ def test_bwd_config_sampled_sets(name, nsets):
             worst[nm] = max(worst[nm], v)
     say("  worst " + " ".join(f"{k}={v:.3e}" for k, v in worst.items()))
     assert max(worst.values()) <= TOL[wl.dtype], worst
+
+
+@pytest.mark.parametrize("path", ["fused", "lines"])
+@pytest.mark.parametrize("scale", [12.0, 60.0])
+def test_bwd_wide_raw_taps(path, scale):
+    """Raw taps far from 0 (sigmoids near 0 or 1; below -25 the fused kernel
+    takes its exact per-tap form, below -40 the line kernels do)."""
+    for (H, W, g) in [(20, 32, 2), (64, 64, 1)]:
+        wl = make_workload(1, 4, H, W, groups=g, cpw=2, dtype="f32", seed=int(scale) + H)
+        wl.w_store = (wl.w_store * np.float32(scale)).astype(np.float32)
+        check(wl, 9, path=path)
 
 
 def test_bwd_ones_invariant():
