@@ -193,7 +193,8 @@ void fused_bwd_kernel(FusedBwdParams prm) {
     // per direction).  The prologue's exact-form branch borrows 4096 floats
     // per wave of the channel-loop planes before they are zeroed.
     constexpr int kSG = kBS * kBS;
-    __shared__ __attribute__((aligned(16))) float lds[5 * kBPlane + 4 * kSG];
+    constexpr int kLoop = (5 * kBPlane + 3) / 4 * 4;     // channel-loop planes, padded
+    __shared__ __attribute__((aligned(16))) float lds[kLoop + 4 * kSG];
     float* const GH = lds;
     float* const HP = lds + kBPlane;   // + d * kBPlane
 
@@ -215,7 +216,10 @@ void fused_bwd_kernel(FusedBwdParams prm) {
     const int L = n / prm.groups;
     const bool has0 = p >= 1 && p < m;
     const bool has2 = p + 1 < m;
-    float* const SG = lds + 5 * kBPlane + d * kSG + p;   // this wave's sums, [slot * 64]
+    float* const SG = lds + kLoop + d * kSG + p;   // this wave's sums, [slot * 64]
+    // per-wave exchange area for one chunk of per-slot registers (prologue
+    // and epilogue only; it lies in the channel-loop planes): [value][slot]
+    float* const XR = lds + d * 4 * 16 * kBS + p;
 
     // slot t <-> line coordinate j
     auto line_of = [&](int t) { return asc ? t : kBS - 1 - t; };
@@ -310,86 +314,87 @@ void fused_bwd_kernel(FusedBwdParams prm) {
 
     // ---- normalised weights of every slot (0 where a slot reads no taps)
     // and the sum S of the sigmoids of its existing taps, kept for the
-    // Jacobian: 1 - sigmoid(a_t) = 1 - w_t S.
+    // Jacobian (s_t = w_t S).
     //   With q_t = 1 + exp(-a_t): w0 = q1 q2 / D, w2 = q0 q1 / D,
     //   D = q1 q2 + q0 q2 + q0 q1 (missing taps: q = 2 and the product
     //   term dropped), S = D / (q0 q1 q2) (a missing tap's q cancels).
-    //   No overflow while every tap is >= -25; otherwise the whole wave
-    //   takes the exact per-tap form.
+    //   No overflow while every tap is >= -25; a chunk with a smaller tap
+    //   is redone with the exact per-tap form.
+    // The work runs as a loop over chunks of 16 slots (compact code: the
+    // whole kernel does not fit the instruction cache unrolled); a chunk's
+    // results reach the statically indexed registers through LDS.
     float w0[kBS], w2[kBS];
+    sfor<0, kBS>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        w0[t] = 0.0f;
+        w2[t] = 0.0f;
+    });
     if (on) {
-        float a[kNCh][3][kChunk];
-#pragma unroll
-        for (int ch = 0; ch < kNCh; ++ch) load_taps(ch * kChunk, a[ch]);
         const float kNegLog2e = -1.44269504088896340736f;
-        float amin = 0.0f;
-        sfor<0, kBS>([&](auto tc) {
-            constexpr int t = decltype(tc)::value;
-            constexpr int ch = t / kChunk, i = t % kChunk;
-            const bool cpl = (coupled >> t) & 1u;
-            // unused taps (missing neighbours, unused lines) are taken as 0
-            const float a0 = cpl && has0 ? a[ch][0][i] : 0.0f;
-            const float a1 = cpl ? a[ch][1][i] : 0.0f;
-            const float a2 = cpl && has2 ? a[ch][2][i] : 0.0f;
-            amin = fminf(amin, fminf(fminf(a0, a1), a2));
-            const float q0 = 1.0f + fast_exp2(a0 * kNegLog2e);
-            const float q1 = 1.0f + fast_exp2(a1 * kNegLog2e);
-            const float q2 = 1.0f + fast_exp2(a2 * kNegLog2e);
-            const float p12 = has0 ? q1 * q2 : 0.0f;
-            const float p01 = has2 ? q0 * q1 : 0.0f;
-            const float D = fmaf(q0, q2, p12) + p01;
-            const float inv = fast_rcp(D);
-            w0[t] = cpl ? p12 * inv : 0.0f;
-            w2[t] = cpl ? p01 * inv : 0.0f;
-            SG[t * kBS] = D * fast_rcp(q0 * q1 * q2);
-        });
-        if (__builtin_amdgcn_ballot_w64(amin < -25.0f) != 0) {
-            // exact form, slot by slot, through this wave's scratch area
-            float* const X0 = lds + d * kSG + p;   // 4096 floats per wave
-            for (int ch = 0; ch < kNCh; ++ch) {
-                float b3[3][kChunk];
-                load_taps(ch * kChunk, b3);
+        for (int ch = 0; ch < kNCh; ++ch) {
+            const int t0 = ch * kChunk;
+            float a[3][kChunk];
+            load_taps(t0, a);
+            float amin = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                const int t = t0 + i;
+                const bool cpl = (coupled >> t) & 1u;
+                // unused taps (missing neighbours, unused lines) are taken as 0
+                const float a0 = cpl && has0 ? a[0][i] : 0.0f;
+                const float a1 = cpl ? a[1][i] : 0.0f;
+                const float a2 = cpl && has2 ? a[2][i] : 0.0f;
+                amin = fminf(amin, fminf(fminf(a0, a1), a2));
+                const float q0 = 1.0f + fast_exp2(a0 * kNegLog2e);
+                const float q1 = 1.0f + fast_exp2(a1 * kNegLog2e);
+                const float q2 = 1.0f + fast_exp2(a2 * kNegLog2e);
+                const float p12 = has0 ? q1 * q2 : 0.0f;
+                const float p01 = has2 ? q0 * q1 : 0.0f;
+                const float D = fmaf(q0, q2, p12) + p01;
+                const float inv = fast_rcp(D);
+                XR[i * kBS] = cpl ? p12 * inv : 0.0f;
+                XR[(kChunk + i) * kBS] = cpl ? p01 * inv : 0.0f;
+                SG[t * kBS] = D * fast_rcp(q0 * q1 * q2);
+            }
+            if (__builtin_amdgcn_ballot_w64(amin < -25.0f) != 0) {
+                // exact form for this chunk
                 for (int i = 0; i < kChunk; ++i) {
-                    const int t = ch * kChunk + i;
+                    const int t = t0 + i;
                     const bool cpl = (coupled >> t) & 1u;
-                    const float a0 = cpl && has0 ? b3[0][i] : 0.0f;
-                    const float a1 = cpl ? b3[1][i] : 0.0f;
-                    const float a2 = cpl && has2 ? b3[2][i] : 0.0f;
+                    float v3[3];
+#pragma unroll
+                    for (int u = 0; u < 3; ++u) v3[u] = a[u][0];
+#pragma unroll
+                    for (int ii = 1; ii < kChunk; ++ii)   // a[.][i] without a dynamic index
+                        if (ii == i)
+#pragma unroll
+                            for (int u = 0; u < 3; ++u) v3[u] = a[u][ii];
+                    const float a0 = cpl && has0 ? v3[0] : 0.0f;
+                    const float a1 = cpl ? v3[1] : 0.0f;
+                    const float a2 = cpl && has2 ? v3[2] : 0.0f;
                     const Taps tp = normalise_taps(a0, a1, a2, has0, has2);
                     const float s0 = has0 ? fast_rcp(1.0f + fast_exp2(a0 * kNegLog2e)) : 0.0f;
                     const float s1 = fast_rcp(1.0f + fast_exp2(a1 * kNegLog2e));
                     const float s2 = has2 ? fast_rcp(1.0f + fast_exp2(a2 * kNegLog2e)) : 0.0f;
                     SG[t * kBS] = (s0 + s1) + s2;
-                    X0[t * kBS] = cpl ? tp.w0 : 0.0f;
+                    XR[i * kBS] = cpl ? tp.w0 : 0.0f;
+                    XR[(kChunk + i) * kBS] = cpl ? tp.w2 : 0.0f;
                 }
             }
-            sfor<0, kBS>([&](auto tc) {
-                constexpr int t = decltype(tc)::value;
-                w0[t] = X0[t * kBS];
-            });
-            for (int ch = 0; ch < kNCh; ++ch) {
-                float b3[3][kChunk];
-                load_taps(ch * kChunk, b3);
-                for (int i = 0; i < kChunk; ++i) {
-                    const int t = ch * kChunk + i;
-                    const bool cpl = (coupled >> t) & 1u;
-                    const float a0 = cpl && has0 ? b3[0][i] : 0.0f;
-                    const float a1 = cpl ? b3[1][i] : 0.0f;
-                    const float a2 = cpl && has2 ? b3[2][i] : 0.0f;
-                    X0[t * kBS] = cpl ? normalise_taps(a0, a1, a2, has0, has2).w2 : 0.0f;
-                }
+            // the chunk's weights into registers (one static block per chunk)
+            switch (ch) {
+#define GSPN_UNDUMP(CH)                                                     \
+                case CH:                                                    \
+                    sfor<0, kChunk>([&](auto ic) {                          \
+                        constexpr int i = decltype(ic)::value;              \
+                        w0[CH * kChunk + i] = XR[i * kBS];                  \
+                        w2[CH * kChunk + i] = XR[(kChunk + i) * kBS];       \
+                    });                                                     \
+                    break;
+                GSPN_UNDUMP(0) GSPN_UNDUMP(1) GSPN_UNDUMP(2) GSPN_UNDUMP(3)
+#undef GSPN_UNDUMP
             }
-            sfor<0, kBS>([&](auto tc) {
-                constexpr int t = decltype(tc)::value;
-                w2[t] = X0[t * kBS];
-            });
         }
-    } else {
-        sfor<0, kBS>([&](auto tc) {
-            constexpr int t = decltype(tc)::value;
-            w0[t] = 0.0f;
-            w2[t] = 0.0f;
-        });
     }
     float e0[kBS], e2[kBS];
     sfor<0, kBS>([&](auto tc) {
@@ -407,25 +412,38 @@ void fused_bwd_kernel(FusedBwdParams prm) {
     const int nvalid = min(N, W - col0);
     const bool t_active = tr < rpi;
     auto row_ok = [&](int it) { return t_active && tr + it * rpi < H; };
-    auto row_off = [&](int it) { return min(tr + it * rpi, H - 1) * W + col0; };   // clamped
-    auto plane_off = [&](int it) { return (tr + it * rpi + 1) * kBPitch + col0 + 1; };
+    // offsets are recomputed from an opaque value at each use, so that the
+    // compiler does not keep them (and their per-element variants) in
+    // registers across the channel loop
+    auto opaque_int = [](int x) {
+        asm volatile("" : "+v"(x));
+        return x;
+    };
+    auto row_off = [&](int it) { return opaque_int(min(tr + it * rpi, H - 1) * W + col0); };   // clamped
+    auto plane_off = [&](int it) { return opaque_int((tr + it * rpi + 1) * kBPitch + col0 + 1); };
     // sum of the four direction planes at LDS offset o, in the order TB, BT,
     // LR, RL (a disabled direction's plane stays zero); no branch, so the
     // reads of a phase are all in flight together
     auto plane_sum = [&](int o) {
         return ((HP[o] + HP[kBPlane + o]) + HP[2 * kBPlane + o]) + HP[3 * kBPlane + o];
     };
-    // x, lam, u, gy rows of channel c (rows past H read a clamped row)
+    // x, lam, u, gy rows of channel c (rows past H read a clamped row); the
+    // slice base is uniform and the lane offset 32-bit, so the accesses use
+    // a scalar base address
     auto load_channel = [&](int c, uint4 (&xr)[kIt], uint4 (&lr)[kIt], uint4 (&ur)[kIt], uint4 (&gr)[kIt]) {
         const size_t so = ((size_t)b * C + c) * (size_t)HW;
+        const T* xs = static_cast<const T*>(prm.x) + so;
+        const T* ls = static_cast<const T*>(prm.lam) + so;
+        const T* us = static_cast<const T*>(prm.u) + so;
+        const T* gs = static_cast<const T*>(prm.gy) + so;
 #pragma unroll
         for (int it = 0; it < kIt; ++it) {
             const int o = row_off(it);
             const bool ok = VEC || row_ok(it);
-            xr[it] = ok ? ld_row(static_cast<const T*>(prm.x) + so + o, nvalid, VEC) : make_uint4(0, 0, 0, 0);
-            lr[it] = ok ? ld_row(static_cast<const T*>(prm.lam) + so + o, nvalid, VEC) : make_uint4(0, 0, 0, 0);
-            ur[it] = ok ? ld_row(static_cast<const T*>(prm.u) + so + o, nvalid, VEC) : make_uint4(0, 0, 0, 0);
-            gr[it] = ok ? ld_row(static_cast<const T*>(prm.gy) + so + o, nvalid, VEC) : make_uint4(0, 0, 0, 0);
+            xr[it] = ok ? ld_row(xs + o, nvalid, VEC) : make_uint4(0, 0, 0, 0);
+            lr[it] = ok ? ld_row(ls + o, nvalid, VEC) : make_uint4(0, 0, 0, 0);
+            ur[it] = ok ? ld_row(us + o, nvalid, VEC) : make_uint4(0, 0, 0, 0);
+            gr[it] = ok ? ld_row(gs + o, nvalid, VEC) : make_uint4(0, 0, 0, 0);
         }
     };
 
@@ -434,7 +452,8 @@ void fused_bwd_kernel(FusedBwdParams prm) {
     load_channel(c_begin, xc, lc, uc, gc);
     lds_barrier();   // every wave has its weights: the scratch area is free
     // zero the channel loop's planes (borders and entries outside the grid stay 0)
-    for (int i = tid; i < 5 * kBPlane; i += kBThreads) lds[i] = 0.0f;
+    for (int i = tid; i < kLoop / 4; i += kBThreads)
+        reinterpret_cast<float4*>(lds)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     lds_barrier();
 
     // 1 for an enabled direction, 0 for a disabled one (whose plane stays 0)
@@ -444,6 +463,9 @@ void fused_bwd_kernel(FusedBwdParams prm) {
 
     for (int c = c_begin; c < c_end; ++c) {
         const size_t so = ((size_t)b * C + c) * (size_t)HW;
+        T* const gus = static_cast<T*>(prm.gu) + so;
+        T* const gxs = static_cast<T*>(prm.gx) + so;
+        T* const gls = static_cast<T*>(prm.glam) + so;
         // lam * x into each enabled direction's plane (the forward then
         // overwrites it in place with h), gy * u into GH
 #pragma unroll
@@ -485,7 +507,7 @@ void fused_bwd_kernel(FusedBwdParams prm) {
                 const int po = plane_off(it);
 #pragma unroll
                 for (int e = 0; e < N; ++e) out[e] = gv[e] * plane_sum(po + e);
-                st_row(static_cast<T*>(prm.gu) + so + row_off(it), out, nvalid, VEC);
+                st_row(gus + row_off(it), out, nvalid, VEC);
             }
         }
         lds_barrier();
@@ -508,8 +530,8 @@ void fused_bwd_kernel(FusedBwdParams prm) {
                     ox[e] = lv[e] * sg;
                     ol[e] = xv[e] * sg;
                 }
-                st_row(static_cast<T*>(prm.gx) + so + row_off(it), ox, nvalid, VEC);
-                st_row(static_cast<T*>(prm.glam) + so + row_off(it), ol, nvalid, VEC);
+                st_row(gxs + row_off(it), ox, nvalid, VEC);
+                st_row(gls + row_off(it), ol, nvalid, VEC);
             }
         }
 #pragma unroll
@@ -528,23 +550,37 @@ void fused_bwd_kernel(FusedBwdParams prm) {
     // and ga_t = w_t (1 - s_t) (D_t - sum_v w_v D_v).  Every weight is
     // formed directly (w1 = s1 / S), and 1 - s_t without cancellation:
     // 1 - s_t for s_t < 1/2, else exp(-a_t) s_t, with s_t = w_t S; so the raw
-    // taps are read again (chunk by chunk, the next chunk in flight).
+    // taps are read again.  Loop over chunks of 16 slots, as the prologue.
     if (on) {
         T* gwd = static_cast<T*>(prm.gw) + ((size_t)(slab * B + b) * Cw + k) * 3 * (size_t)HW;
         const float kNegLog2e = -1.44269504088896340736f;
-        float ab[2][3][kChunk];
-        load_taps(0, ab[0]);
-        sfor<0, kNCh>([&](auto chc) {
-            constexpr int ch = decltype(chc)::value;
-            constexpr int t0 = ch * kChunk;
-            if constexpr (ch + 1 < kNCh) load_taps(t0 + kChunk, ab[(ch + 1) % 2]);
-            const float (&a)[3][kChunk] = ab[ch % 2];
+        for (int ch = 0; ch < kNCh; ++ch) {
+            const int t0 = ch * kChunk;
+            float a[3][kChunk];
+            load_taps(t0, a);
+            // the chunk's registers into LDS (one static block per chunk)
+            switch (ch) {
+#define GSPN_DUMP(CH)                                                       \
+                case CH:                                                    \
+                    sfor<0, kChunk>([&](auto ic) {                          \
+                        constexpr int i = decltype(ic)::value;              \
+                        XR[i * kBS] = w0[CH * kChunk + i];                  \
+                        XR[(kChunk + i) * kBS] = w2[CH * kChunk + i];       \
+                        XR[(2 * kChunk + i) * kBS] = e0[CH * kChunk + i];   \
+                        XR[(3 * kChunk + i) * kBS] = e2[CH * kChunk + i];   \
+                    });                                                     \
+                    break;
+                GSPN_DUMP(0) GSPN_DUMP(1) GSPN_DUMP(2) GSPN_DUMP(3)
+#undef GSPN_DUMP
+            }
             float gaf[3][kChunk];
-            sfor<0, kChunk>([&](auto ic) {
-                constexpr int i = decltype(ic)::value;
-                constexpr int t = t0 + i;
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                const int t = t0 + i;
                 const bool cpl = (coupled >> t) & 1u;
                 const float S = SG[t * kBS];
+                const float x0 = XR[i * kBS], x2 = XR[(kChunk + i) * kBS];
+                const float E0 = XR[(2 * kChunk + i) * kBS], E2 = XR[(3 * kChunk + i) * kBS];
                 const float av[3] = {cpl && has0 ? a[0][i] : 0.0f, cpl ? a[1][i] : 0.0f,
                                      cpl && has2 ? a[2][i] : 0.0f};
                 float ex[3];
@@ -553,21 +589,20 @@ void fused_bwd_kernel(FusedBwdParams prm) {
                 // w1 = sigmoid(a1) / S; if every sigmoid underflows, the
                 // weights came from the exact form and w1 = 1 - w0 - w2
                 const float w1d = fast_rcp(1.0f + ex[1]) * fast_rcp(S);
-                const float wv[3] = {w0[t], S > 1e-30f ? w1d : 1.0f - w0[t] - w2[t], w2[t]};
+                const float wv[3] = {x0, S > 1e-30f ? w1d : 1.0f - x0 - x2, x2};
                 float om[3];
 #pragma unroll
                 for (int u = 0; u < 3; ++u) {
                     const float sg = wv[u] * S;
                     om[u] = sg < 0.5f ? 1.0f - sg : ex[u] * sg;
                 }
-                const float E0 = e0[t], E2 = e2[t];
                 const float r0 = fmaf(wv[1], E0, wv[2] * (E0 - E2));
                 const float r1 = -fmaf(wv[0], E0, wv[2] * E2);
                 const float r2 = fmaf(wv[1], E2, wv[0] * (E2 - E0));
                 gaf[0][i] = cpl ? wv[0] * om[0] * r0 : 0.0f;
                 gaf[1][i] = cpl ? wv[1] * om[1] * r1 : 0.0f;
                 gaf[2][i] = cpl ? wv[2] * om[2] * r2 : 0.0f;
-            });
+            }
             if (col_vec) {
                 // lane p writes its row: the chunk's columns as 16-byte vectors
                 const int c0 = chunk_col0(t0);
@@ -596,7 +631,7 @@ void fused_bwd_kernel(FusedBwdParams prm) {
                     }
                 }
             }
-        });
+        }
     }
 }
 
