@@ -47,11 +47,23 @@ sys.path.insert(0, ROOT)
 METRIC = "GSPN scan GB/s and % of HBM peak (4-dir fwd), 1K C-GSPN config"
 METRIC_BWD = "GSPN scan backward GB/s and % of HBM peak (4-dir bwd)"
 HBM_PEAK_GBPS = 8000.0
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fused_scan_kernel_cgspn1k_traffic.txt")
-PROFILE_STATS = os.path.join(ROOT, "profiles", "fused_scan_kernel_cgspn1k_stats.txt")
 COPY_CALIBRATION_BYTES = 256 * 1024 * 1024
-KERNEL_SOURCES = ["linear_spatial_propagation_amd/csrc/gspn_fused.hip",
-                  "linear_spatial_propagation_amd/csrc/gspn_device.h"]
+# The dominant kernel of each pass on the default workload (C-GSPN 1K, 64 x 64
+# grids: one fused kernel per call), the sources its code comes from, and its
+# committed rocprofv3 summaries.
+PASSES = {
+    "fwd": {"kernel": "fused_scan_kernel",
+            "sources": ["linear_spatial_propagation_amd/csrc/gspn_fused.hip",
+                        "linear_spatial_propagation_amd/csrc/gspn_device.h"]},
+    "bwd": {"kernel": "fused_bwd_kernel",
+            "sources": ["linear_spatial_propagation_amd/csrc/gspn_fused_bwd.hip",
+                        "linear_spatial_propagation_amd/csrc/gspn_lines.h",
+                        "linear_spatial_propagation_amd/csrc/gspn_device.h"]},
+}
+
+
+def profile_path(pass_, what, config="cgspn1k"):
+    return os.path.join(ROOT, "profiles", f"{PASSES[pass_]['kernel']}_{config}_{what}.txt")
 
 
 def algorithmic_bytes(B, C, H, W, dirs, groups, cpw, dtype) -> int:
@@ -74,9 +86,9 @@ def algorithmic_bytes_bwd(B, C, H, W, dirs, groups, cpw, dtype) -> int:
     return 7 * E * s + fwd_taps + s * nd * B * (C // cpw) * 3 * H * W
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(pass_="fwd") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in PASSES[pass_]["sources"]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -96,11 +108,11 @@ def _read_summary(path):
     return out
 
 
-def load_traffic():
+def load_traffic(pass_="fwd"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when the kernel source changed since the counters were taken."""
-    t = _read_summary(PROFILE_TRAFFIC)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    t = _read_summary(profile_path(pass_, "traffic"))
+    if t.get("kernel_source_hash") != kernel_source_hash(pass_):
         return None
     try:
         return int(float(t["hbm_bytes_per_launch"]))
@@ -109,6 +121,10 @@ def load_traffic():
 
 
 def _kernel_short(name):
+    for k in ("fused_scan_kernel", "fused_bwd_kernel", "adjoint_scan_kernel", "line_scan_kernel",
+              "transpose_kernel", "convert_kernel"):
+        if k in name:
+            return k
     if "fused_scan_kernel" in name:
         return "fused_scan_kernel"
     if "direction_kernel" in name:
@@ -120,7 +136,7 @@ def _kernel_short(name):
     return name[:48]
 
 
-def summarize_pmc(pmc_dir, command, config="cgspn1k"):
+def summarize_pmc(pmc_dir, command, config="cgspn1k", pass_="fwd"):
     """Summarise two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) of a bench
     run with --copy-calibration into the traffic summary under profiles/.
 
@@ -146,19 +162,21 @@ def summarize_pmc(pmc_dir, command, config="cgspn1k"):
         copy_f = max(v for _, v in vals[("FETCH_SIZE", "copy")])
     copy_kib = COPY_CALIBRATION_BYTES / 1024
     f_scale, w_scale = copy_kib / copy_f, copy_kib / copy_w
-    fk = [v for _, v in vals[("FETCH_SIZE", "fused_scan_kernel")]]
-    wk = [v for _, v in vals[("WRITE_SIZE", "fused_scan_kernel")]]
+    kname = PASSES[pass_]["kernel"]
+    fk = [v for _, v in vals[("FETCH_SIZE", kname)]]
+    wk = [v for _, v in vals[("WRITE_SIZE", kname)]]
     fetch_kib, write_kib = sum(fk) / len(fk), sum(wk) / len(wk)
     hbm = fetch_kib * 1024 * f_scale + write_kib * 1024 * w_scale
     c = CONFIGS[config]
-    alg = algorithmic_bytes(c["B"], c["C"], c["H"], c["W"], 15, c["groups"], c["cpw"], c["dtype"])
+    alg = (algorithmic_bytes_bwd if pass_ == "bwd" else algorithmic_bytes)(
+        c["B"], c["C"], c["H"], c["W"], 15, c["groups"], c["cpw"], c["dtype"])
     lines = [
-        f"# rocprofv3 memory counters: fused_scan_kernel<bf16> on {config} "
+        f"# rocprofv3 memory counters: {kname}<bf16> on {config} "
         f"(B={c['B']} C={c['C']} H={c['H']} W={c['W']} groups={c['groups']} ch_per_weight={c['cpw']} {c['dtype']})",
         f"# command (two passes, FETCH_SIZE then WRITE_SIZE): {command}",
         "# FETCH_SIZE and WRITE_SIZE are KiB per dispatch, averaged over the kernel's dispatches;",
         "# each is scaled by (known bytes / counter bytes) of a 256 MiB device-to-device copy in the same run.",
-        f"kernel_source_hash: {kernel_source_hash()}",
+        f"kernel_source_hash: {kernel_source_hash(pass_)}",
         f"dispatches: {len(fk)}",
         f"fetch_kib_per_dispatch: {fetch_kib:.1f}",
         f"write_kib_per_dispatch: {write_kib:.1f}",
@@ -173,12 +191,12 @@ def summarize_pmc(pmc_dir, command, config="cgspn1k"):
         f"algorithmic_bytes_per_launch: {alg}",
         f"traffic_over_algorithmic: {hbm / alg:.4f}",
     ]
-    with open(PROFILE_TRAFFIC, "w") as f:
+    with open(profile_path(pass_, "traffic", config), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def summarize_stats(stats_csv, command, config="cgspn1k"):
+def summarize_stats(stats_csv, command, config="cgspn1k", pass_="fwd"):
     """Copy the kernel rows of a rocprofv3 --kernel-trace --stats CSV into the
     stats summary under profiles/."""
     import csv
@@ -189,8 +207,8 @@ def summarize_stats(stats_csv, command, config="cgspn1k"):
     for r in rows:
         lines.append(f"{_kernel_short(r['Name'])}, {r['Calls']}, {r['TotalDurationNs']}, "
                      f"{float(r['AverageNs']):.1f}, {r['MinNs']}, {r['MaxNs']}, {float(r['Percentage']):.2f}")
-    lines.append(f"kernel_source_hash: {kernel_source_hash()}")
-    with open(PROFILE_STATS, "w") as f:
+    lines.append(f"kernel_source_hash: {kernel_source_hash(pass_)}")
+    with open(profile_path(pass_, "stats", config), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -254,10 +272,10 @@ def main():
     ap.add_argument("--profile-command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc, args.profile_command, args.config)
+        summarize_pmc(args.summarize_pmc, args.profile_command, args.config, args.pass_)
         return
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats, args.profile_command, args.config)
+        summarize_stats(args.summarize_stats, args.profile_command, args.config, args.pass_)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this operator has no cross-GPU step, and runs "
@@ -348,7 +366,7 @@ def main():
     value = nbytes * args.steps / elapsed / 1e9
     avg_launch = float(per.mean())
     achieved = nbytes / avg_launch / 1e9
-    traffic = load_traffic() if args.config == "cgspn1k" and not bwd else None
+    traffic = load_traffic(args.pass_) if args.config == "cgspn1k" else None
     E = B * C * H * W
     out = {
         "metric": METRIC_BWD if bwd else METRIC,
@@ -367,7 +385,7 @@ def main():
             "workload": f"{args.config}: B={B} C={C} H={H} W={W} groups={wl.groups} "
                         f"ch_per_weight={wl.cpw} dirs=TB|BT|LR|RL, {wl.dtype} I/O, fp32 arithmetic",
             "io_dtype": wl.dtype,
-            "path": "backward line kernels" if bwd else
+            "path": ("fused backward" if max(H, W) <= 64 else "backward line kernels") if bwd else
                     {1: "fused", 2: "general"}[gspn.select_path(B, C, H, W, groups=wl.groups,
                                                                 ch_per_weight=wl.cpw)],
             "algorithmic_bytes_per_step": nbytes,
@@ -385,7 +403,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
     }
     if bwd:
-        out["roofline"]["kernel"] = "gspn_scan_bwd, all launches of one call"
+        # 64 x 64 grids and smaller: one fused kernel per call
+        out["roofline"]["kernel"] = ("fused_bwd_kernel" if max(H, W) <= 64
+                                     else "gspn_scan_bwd, all launches of one call")
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args.config, backward=bwd)
     print(json.dumps(out), flush=True)
