@@ -30,6 +30,11 @@ consumes, gx, glam, gu once and the whole tap-gradient tensor once:
     + s * ndir * B * Cw * 3 * H * W.
 Its roofline object covers the whole call (all of its launches).
 
+With --variant dirs a step is one call of gspn_scan_fwd_ex with lambda and
+u per direction (y = sum_d u_d * h_d); the algorithmic bytes count the four
+lambda and four u slabs once:
+    s * (|x| + ndir |lam| + ndir |u| + |y|) + (taps as for the forward).
+
 Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -46,6 +51,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GSPN scan GB/s and % of HBM peak (4-dir fwd), 1K C-GSPN config"
 METRIC_BWD = "GSPN scan backward GB/s and % of HBM peak (4-dir bwd)"
+METRIC_DIRS = "GSPN scan GB/s and % of HBM peak (4-dir fwd, per-direction lambda and u)"
 HBM_PEAK_GBPS = 8000.0
 COPY_CALIBRATION_BYTES = 256 * 1024 * 1024
 # The dominant kernel of each pass on the default workload (C-GSPN 1K, 64 x 64
@@ -262,6 +268,8 @@ def main():
     ap.add_argument("--config", default="cgspn1k")
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the backward")
+    ap.add_argument("--variant", choices=("none", "dirs"), default="none",
+                    help="dirs: the forward with per-direction lambda and u (gspn_scan_fwd_ex)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for counter calibration)")
@@ -300,8 +308,18 @@ def main():
         return (t.view(torch.bfloat16) if wl.dtype == "bf16" else t).to(dev)
 
     bwd = args.pass_ == "bwd"
+    dirs_variant = args.variant == "dirs" and not bwd
     base = [up(a) for a in (wl.x_store, wl.w_store, wl.lam_store, wl.u_store)]
-    if bwd:
+    if dirs_variant:
+        # per-direction lambda and u: U(0, 1), seeded, in the workload's dtype
+        from linear_spatial_propagation_amd.inputs import _store
+        rng = np.random.default_rng([cfgd["seed"], 5])
+        for i in (2, 3):
+            base[i] = up(_store(rng.random((4, B, C, H, W), dtype=np.float32), wl.dtype))
+        E0 = B * C * H * W
+        nbytes = algorithmic_bytes(B, C, H, W, 15, wl.groups, wl.cpw, wl.dtype) + 6 * E0 * (2 if wl.dtype == "bf16" else 4)
+        outs_like = [base[0]]
+    elif bwd:
         from linear_spatial_propagation_amd.inputs import make_gy
         base.append(up(make_gy(wl, 1000 + cfgd["seed"])))
         nbytes = algorithmic_bytes_bwd(B, C, H, W, 15, wl.groups, wl.cpw, wl.dtype)
@@ -321,6 +339,8 @@ def main():
         ins, outs = sets[i % R]
         if bwd:
             gspn.scan_bwd(*ins, dirs=15, groups=wl.groups, ch_per_weight=wl.cpw, out=outs)
+        elif dirs_variant:
+            gspn.scan_fwd_dirs(*ins, dirs=15, groups=wl.groups, ch_per_weight=wl.cpw, out=outs[0])
         else:
             gspn.scan_fwd(*ins, dirs=15, groups=wl.groups, ch_per_weight=wl.cpw, out=outs[0])
 
@@ -366,10 +386,10 @@ def main():
     value = nbytes * args.steps / elapsed / 1e9
     avg_launch = float(per.mean())
     achieved = nbytes / avg_launch / 1e9
-    traffic = load_traffic(args.pass_) if args.config == "cgspn1k" else None
+    traffic = load_traffic(args.pass_) if args.config == "cgspn1k" and not dirs_variant else None
     E = B * C * H * W
     out = {
-        "metric": METRIC_BWD if bwd else METRIC,
+        "metric": METRIC_BWD if bwd else (METRIC_DIRS if dirs_variant else METRIC),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -386,6 +406,7 @@ def main():
                         f"ch_per_weight={wl.cpw} dirs=TB|BT|LR|RL, {wl.dtype} I/O, fp32 arithmetic",
             "io_dtype": wl.dtype,
             "path": ("fused backward" if max(H, W) <= 64 else "backward line kernels") if bwd else
+                    "line kernels, per-direction lambda and u" if dirs_variant else
                     {1: "fused", 2: "general"}[gspn.select_path(B, C, H, W, groups=wl.groups,
                                                                 ch_per_weight=wl.cpw)],
             "algorithmic_bytes_per_step": nbytes,
@@ -402,11 +423,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
     }
+    if dirs_variant:
+        out["roofline"]["kernel"] = "gspn_scan_fwd_ex, all launches of one call"
     if bwd:
         # 64 x 64 grids and smaller: one fused kernel per call
         out["roofline"]["kernel"] = ("fused_bwd_kernel" if max(H, W) <= 64
                                      else "gspn_scan_bwd, all launches of one call")
-    if not args.no_cpu:
+    if not args.no_cpu and not dirs_variant:
         out["cpu_baseline"] = cpu_baseline(args.config, backward=bwd)
     print(json.dumps(out), flush=True)
 

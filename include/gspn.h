@@ -109,7 +109,14 @@ enum {
     GSPN_ERR_ALIGN = -7,  /* a base pointer is not 16-byte aligned */
     GSPN_ERR_ALIAS = -8,  /* an output overlaps an input or another output */
     GSPN_ERR_HIP = -9,    /* a HIP call failed; see gspn_last_error() */
-    GSPN_ERR_PATH = -10   /* unknown path, or the path (or the backward) cannot take this shape */
+    GSPN_ERR_PATH = -10,  /* unknown path, or the path (or the backward) cannot take this shape */
+    GSPN_ERR_FLAGS = -11  /* unknown bit in flags (gspn_scan_fwd_ex) */
+};
+
+/* Flags of gspn_scan_fwd_ex. */
+enum {
+    GSPN_LAM_PER_DIR = 1, /* lam holds one [B][C][H][W] slab per enabled direction */
+    GSPN_U_PER_DIR = 2    /* u holds one slab per enabled direction: y = sum_d u_d * h_d */
 };
 
 /* Largest H and W accepted. */
@@ -145,6 +152,27 @@ int gspn_scan_fwd(const void *x, const void *w_raw, const void *lam, const void 
 int gspn_scan_fwd_path(const void *x, const void *w_raw, const void *lam, const void *u, void *y,
                        int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
                        int32_t ch_per_weight, int32_t dtype, int32_t path, hipStream_t stream);
+
+/*
+ * Variants of the forward with per-direction gains and gates:
+ *   y = sum over enabled d of u_d (.) h_d,   h_d the scan of direction d driven
+ *   by lam_d (.) x (otherwise exactly the definition above).
+ * The pages index neither lam nor u by direction ("Key design 1"), so
+ * gspn_scan_fwd shares them; "Key design 2" merges the directions with a
+ * "learnable merger", which a per-direction gate u_d realises elementwise
+ * (per-channel direction weights are the case of u_d constant over H, W).
+ *   flags : GSPN_LAM_PER_DIR and/or GSPN_U_PER_DIR; a flagged tensor has
+ *           shape [popcount(dirs)][B][C][H][W], slabs in ascending bit order.
+ *           flags = 0 is gspn_scan_fwd.
+ * Other arguments, layouts and errors as gspn_scan_fwd; unknown flag bits
+ * give GSPN_ERR_FLAGS.  With a flag set the call runs the line kernels
+ * (H, W <= 512 and multiples of K, else GSPN_ERR_PATH) and, with
+ * GSPN_LAM_PER_DIR and LR or RL enabled, its workspace holds one transposed
+ * lam per column direction.  No backward is provided for the variants.
+ */
+int gspn_scan_fwd_ex(const void *x, const void *w_raw, const void *lam, const void *u, void *y,
+                     int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
+                     int32_t ch_per_weight, uint32_t flags, int32_t dtype, hipStream_t stream);
 
 /* The path gspn_scan_fwd would take for these sizes (GSPN_PATH_FUSED or
  * GSPN_PATH_GENERAL), or a negative error code for invalid sizes. */

@@ -2,6 +2,7 @@
 
     y = scan_fwd(x, w_raw, lam, u, dirs=15, groups=1, ch_per_weight=1)
     gx, gw_raw, glam, gu = scan_bwd(x, w_raw, lam, u, gy, dirs=15, groups=1, ch_per_weight=1)
+    y = scan_fwd_dirs(x, w_raw, lam_d, u_d, ...)   # per-direction gains / gates
 
 computes the 4-direction line recurrence of the Generalized Spatial
 Propagation Network with hand-written HIP kernels (libgspn.so, C ABI in
@@ -18,7 +19,7 @@ from . import _lib
 from ._lib import (DIR_ALL, DIR_BT, DIR_LR, DIR_RL, DIR_TB, PATH_AUTO, PATH_FUSED, PATH_GENERAL,
                    GspnError, load, select_path)
 
-__all__ = ["scan_fwd", "scan_bwd", "select_path", "load", "GspnError", "DIR_TB", "DIR_BT", "DIR_LR", "DIR_RL",
+__all__ = ["scan_fwd", "scan_bwd", "scan_fwd_dirs", "select_path", "load", "GspnError", "DIR_TB", "DIR_BT", "DIR_LR", "DIR_RL",
            "DIR_ALL", "PATH_AUTO", "PATH_FUSED", "PATH_GENERAL"]
 
 
@@ -88,6 +89,46 @@ def scan_bwd(x, w_raw, lam, u, gy, *, dirs: int = DIR_ALL, groups: int = 1, ch_p
                                stream=stream)
     _lib.check(rc)
     return gx, gw, glam, gu
+
+
+def scan_fwd_dirs(x, w_raw, lam, u, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1,
+                  out=None):
+    """Forward scan with per-direction lambda and/or u (gspn_scan_fwd_ex).
+
+    lam and u are each either [B, C, H, W] (shared by the directions) or
+    [popcount(dirs), B, C, H, W] (one slab per enabled direction, ascending
+    bit order); y = sum_d u_d * h_d with h_d driven by lam_d * x.
+    """
+    import torch
+    if x.dim() != 4:
+        raise ValueError("x must be [B, C, H, W]")
+    nd = bin(dirs & 15).count("1")
+    flags = 0
+    shared = {"x": x, "w_raw": w_raw}
+    for name, t, bit in (("lam", lam, _lib.LAM_PER_DIR), ("u", u, _lib.U_PER_DIR)):
+        if t.dim() == 5:
+            if tuple(t.shape) != (nd,) + tuple(x.shape):
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(nd,) + tuple(x.shape)}")
+            flags |= bit
+            shared[name] = t[0]       # shape and dtype checks on one slab
+        else:
+            shared[name] = t
+    dev, (B, C, H, W) = _check_inputs(shared, dirs, ch_per_weight)
+    for name, t in (("lam", lam), ("u", u)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or out.device != dev or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = _lib.scan_fwd_ex_ptr(x.data_ptr(), w_raw.data_ptr(), lam.data_ptr(), u.data_ptr(),
+                                  out.data_ptr(), B, C, H, W, dirs=dirs, groups=groups,
+                                  ch_per_weight=ch_per_weight, flags=flags, dtype=_dtype_code(x),
+                                  stream=stream)
+    _lib.check(rc)
+    return out
 
 
 def scan_fwd(x, w_raw, lam, u, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1,

@@ -20,7 +20,9 @@ PATH_FUSED = 1
 PATH_GENERAL = 2
 DIR_TB, DIR_BT, DIR_LR, DIR_RL, DIR_ALL = 1, 2, 4, 8, 15
 
-EXPORTED = ("gspn_scan_fwd", "gspn_scan_fwd_path", "gspn_select_path", "gspn_scan_bwd",
+LAM_PER_DIR, U_PER_DIR = 1, 2
+
+EXPORTED = ("gspn_scan_fwd", "gspn_scan_fwd_path", "gspn_scan_fwd_ex", "gspn_select_path", "gspn_scan_bwd",
             "gspn_scan_bwd_path", "gspn_bwd_supported", "gspn_status_string", "gspn_last_error", "gspn_version")
 
 _lock = threading.Lock()
@@ -49,6 +51,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.gspn_scan_fwd_path.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, u32, i32, i32, i32,
                                            i32, vp]
         lib.gspn_scan_fwd_path.restype = ctypes.c_int
+        lib.gspn_scan_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, u32, i32, i32, u32, i32, vp]
+        lib.gspn_scan_fwd_ex.restype = ctypes.c_int
         lib.gspn_select_path.argtypes = [i64, i64, i64, i64, u32, i32, i32, i32]
         lib.gspn_select_path.restype = ctypes.c_int
         lib.gspn_scan_bwd.argtypes = [vp] * 9 + [i64, i64, i64, i64, u32, i32, i32, i32, vp]
@@ -85,6 +89,14 @@ def scan_fwd_ptr(x: int, w: int, lam: int, u: int, y: int, B: int, C: int, H: in
     """Raw call on device pointers; returns the status code."""
     return load().gspn_scan_fwd_path(x, w, lam, u, y, B, C, H, W, dirs, groups, ch_per_weight,
                                      dtype, path, stream)
+
+
+def scan_fwd_ex_ptr(x: int, w: int, lam: int, u: int, y: int, B: int, C: int, H: int, W: int, *,
+                    dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1, flags: int = 0,
+                    dtype: int = GSPN_BF16, stream: int = 0) -> int:
+    """Raw call of the per-direction variant on device pointers; returns the status code."""
+    return load().gspn_scan_fwd_ex(x, w, lam, u, y, B, C, H, W, dirs, groups, ch_per_weight, flags,
+                                   dtype, stream)
 
 
 def scan_bwd_ptr(x: int, w: int, lam: int, u: int, gy: int, gx: int, gw: int, glam: int, gu: int,

@@ -69,6 +69,7 @@ const char* gspn_status_string(int status) {
         case GSPN_ERR_ALIAS: return "GSPN_ERR_ALIAS: an output overlaps an input or another output";
         case GSPN_ERR_HIP: return "GSPN_ERR_HIP: a HIP call failed (see gspn_last_error)";
         case GSPN_ERR_PATH: return "GSPN_ERR_PATH: unknown path, or the path cannot run this shape";
+        case GSPN_ERR_FLAGS: return "GSPN_ERR_FLAGS: unknown bit in flags";
         default: return "unknown GSPN status";
     }
 }
@@ -79,12 +80,17 @@ int gspn_select_path(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, 
     return rc ? rc : auto_path(H, W);
 }
 
-int gspn_scan_fwd_path(const void* x, const void* w_raw, const void* lam, const void* u, void* y,
-                       int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
-                       int32_t ch_per_weight, int32_t dtype, int32_t path, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int scan_fwd_impl(const void* x, const void* w_raw, const void* lam, const void* u, void* y, int64_t B,
+                  int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups, int32_t ch_per_weight,
+                  uint32_t flags, int32_t dtype, int32_t path, hipStream_t stream) {
     g_last_error[0] = '\0';
     int rc = check_sizes(B, C, H, W, dirs, groups, ch_per_weight, dtype);
     if (rc) return rc;
+    if (flags & ~(uint32_t)(GSPN_LAM_PER_DIR | GSPN_U_PER_DIR)) return GSPN_ERR_FLAGS;
     if (!x || !w_raw || !lam || !u || !y) return GSPN_ERR_NULL;
     const void* ptrs[5] = {x, w_raw, lam, u, y};
     for (const void* q : ptrs)
@@ -93,17 +99,26 @@ int gspn_scan_fwd_path(const void* x, const void* w_raw, const void* lam, const 
     const size_t E = (size_t)B * C * H * W;
     const size_t nbytes = E * es;
     const size_t wbytes = (size_t)popcount4(dirs) * B * (C / ch_per_weight) * 3 * H * W * es;
-    if (overlaps(y, nbytes, x, nbytes) || overlaps(y, nbytes, lam, nbytes) ||
-        overlaps(y, nbytes, u, nbytes) || overlaps(y, nbytes, w_raw, wbytes))
+    const size_t lbytes = (flags & GSPN_LAM_PER_DIR) ? popcount4(dirs) * nbytes : nbytes;
+    const size_t ubytes = (flags & GSPN_U_PER_DIR) ? popcount4(dirs) * nbytes : nbytes;
+    if (overlaps(y, nbytes, x, nbytes) || overlaps(y, nbytes, lam, lbytes) ||
+        overlaps(y, nbytes, u, ubytes) || overlaps(y, nbytes, w_raw, wbytes))
         return GSPN_ERR_ALIAS;
-    if (path == GSPN_PATH_AUTO) path = auto_path(H, W);
+    // per-direction lambda / u run on the line kernels only
+    if (path == GSPN_PATH_AUTO) path = flags ? GSPN_PATH_GENERAL : auto_path(H, W);
     if (path != GSPN_PATH_FUSED && path != GSPN_PATH_GENERAL) return GSPN_ERR_PATH;
-    if (path == GSPN_PATH_FUSED && auto_path(H, W) != GSPN_PATH_FUSED) return GSPN_ERR_PATH;
+    if (path == GSPN_PATH_FUSED && (auto_path(H, W) != GSPN_PATH_FUSED || flags)) return GSPN_ERR_PATH;
+    if (flags && !gspn::lines_supported((int)H, (int)W)) {
+        set_error_text("per-direction lambda / u run on the line kernels: H, W <= 512 and multiples of K");
+        return GSPN_ERR_PATH;
+    }
 
     gspn::ScanArgs a;
     a.x = x; a.w = w_raw; a.lam = lam; a.u = u; a.y = y;
     a.B = (int)B; a.C = (int)C; a.H = (int)H; a.W = (int)W;
     a.dirs = dirs; a.groups = groups; a.cpw = ch_per_weight; a.bf16 = dtype == GSPN_BF16;
+    a.lam_dir = (flags & GSPN_LAM_PER_DIR) != 0;
+    a.u_dir = (flags & GSPN_U_PER_DIR) != 0;
 
     if (path == GSPN_PATH_FUSED) {
         const hipError_t e = gspn::launch_fused(a, stream);
@@ -122,6 +137,24 @@ int gspn_scan_fwd_path(const void* x, const void* w_raw, const void* lam, const 
     if (e != hipSuccess) { set_error("general kernel launch", e); return GSPN_ERR_HIP; }
     if (ef != hipSuccess) { set_error("hipFreeAsync(workspace)", ef); return GSPN_ERR_HIP; }
     return GSPN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gspn_scan_fwd_path(const void* x, const void* w_raw, const void* lam, const void* u, void* y,
+                       int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
+                       int32_t ch_per_weight, int32_t dtype, int32_t path, hipStream_t stream) {
+    return scan_fwd_impl(x, w_raw, lam, u, y, B, C, H, W, dirs, groups, ch_per_weight, 0u, dtype, path,
+                         stream);
+}
+
+int gspn_scan_fwd_ex(const void* x, const void* w_raw, const void* lam, const void* u, void* y, int64_t B,
+                     int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups, int32_t ch_per_weight,
+                     uint32_t flags, int32_t dtype, hipStream_t stream) {
+    return scan_fwd_impl(x, w_raw, lam, u, y, B, C, H, W, dirs, groups, ch_per_weight, flags, dtype,
+                         GSPN_PATH_AUTO, stream);
 }
 
 int gspn_scan_fwd(const void* x, const void* w_raw, const void* lam, const void* u, void* y,
@@ -183,6 +216,7 @@ int gspn_scan_bwd_path(const void* x, const void* w_raw, const void* lam, const 
     g.fwd.x = x; g.fwd.w = w_raw; g.fwd.lam = lam; g.fwd.u = u; g.fwd.y = nullptr;
     g.fwd.B = (int)B; g.fwd.C = (int)C; g.fwd.H = (int)H; g.fwd.W = (int)W;
     g.fwd.dirs = dirs; g.fwd.groups = groups; g.fwd.cpw = ch_per_weight; g.fwd.bf16 = dtype == GSPN_BF16;
+    g.fwd.lam_dir = 0; g.fwd.u_dir = 0;
     g.gy = gy; g.gx = gx; g.gw = gw_raw; g.glam = glam; g.gu = gu;
     if (path == GSPN_PATH_FUSED) {
         const hipError_t e = gspn::launch_fused_bwd(g, stream);

@@ -17,7 +17,9 @@ struct ScanArgs {
     uint32_t dirs;
     int groups;
     int cpw;
-    int bf16;  // 1: bf16 storage, 0: fp32 storage
+    int bf16;     // 1: bf16 storage, 0: fp32 storage
+    int lam_dir;  // 1: lam holds one [B][C][H][W] slab per enabled direction (line path only)
+    int u_dir;    // 1: u holds one slab per enabled direction, y = sum_d u_d h_d (line path only)
 };
 
 // Fused 4-direction kernel: H <= 64 and W <= 64.
@@ -28,7 +30,8 @@ hipError_t launch_fused(const ScanArgs& a, hipStream_t stream);
 // positions per lane, lines_positions_per_lane).  Workspace layout, in
 // order: fp32 planes [nd][B][C][H*W], a 2 KiB sink for idle lanes' stores;
 // if LR or RL is enabled, x and lambda
-// transposed ([B][C][W][H], I/O dtype) and the enabled column directions'
+// transposed ([B][C][W][H], I/O dtype; lambda once per column direction when
+// it is per direction) and the enabled column directions'
 // raw taps transposed ([ncol][B][C/cpw][3][W][H]).
 constexpr int kLinesMaxSide = 512;
 struct LinesWorkspace {

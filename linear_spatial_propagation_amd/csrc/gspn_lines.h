@@ -116,6 +116,8 @@ struct LineParams {
     const void* wT;     // [ncol][B][Cw][3][W][H]
     float* planes;      // [nd][B][C][n_d][m_d], line-major per direction
     float* sink;        // 64 * 8 floats that absorb the stores of idle lanes
+    size_t lam_ds;      // elements between directions' lambda slabs (0: shared)
+    size_t lamT_ds;     // elements between column directions' transposed slabs (0: shared)
     int B, C, H, W, Cw, cpw, groups;
     int nd;
     int dir_of_slot[4];
@@ -182,7 +184,9 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
 
     // every tensor is read as [n][m], line-major
     const T* xs = static_cast<const T*>(is_row ? prm.x : prm.xT) + ((size_t)b * C + c) * HW;
-    const T* ls = static_cast<const T*>(is_row ? prm.lam : prm.lamT) + ((size_t)b * C + c) * HW;
+    const T* ls = (is_row ? static_cast<const T*>(prm.lam) + slot * prm.lam_ds
+                          : static_cast<const T*>(prm.lamT) + prm.col_index[slot] * prm.lamT_ds) +
+                  ((size_t)b * C + c) * HW;
     const T* ws = is_row
         ? static_cast<const T*>(prm.w) + ((size_t)(slot * B + b) * prm.Cw + k) * 3 * HW
         : static_cast<const T*>(prm.wT) + ((size_t)(prm.col_index[slot] * B + b) * prm.Cw + k) * 3 * HW;
@@ -442,6 +446,110 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams prm) {
     }
 }
 
+// y = sum_d u_d * h_d (per-direction gates: the elementwise learnable merger).
+// Same tiling as merge_kernel; u holds one [B][C][H][W] slab per enabled
+// direction (slot order).  The sum runs in slot order (TB, BT, LR, RL); each
+// column plane is transposed through LDS on its own, so that its gate
+// multiplies it at the right pixel.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_dirs_kernel(MergeParams prm) {
+    __shared__ float tile[kTile][kTile + 1];
+    const int t = blockIdx.x;
+    const int tc = t % prm.tiles_c;
+    const int tr = (t / prm.tiles_c) % prm.tiles_r;
+    const size_t bc = (size_t)(t / (prm.tiles_c * prm.tiles_r));
+    const int H = prm.H, W = prm.W;
+    const size_t HW = (size_t)H * W;
+    const size_t E = (size_t)prm.B * prm.C * HW;
+    const int r0 = tr * kTile, c0 = tc * kTile;
+    const T* __restrict__ gu = static_cast<const T*>(prm.in[0]) + bc * HW;
+    T* __restrict__ gy = static_cast<T*>(prm.out[0]) + bc * HW;
+
+    if (r0 + kTile <= H && c0 + kTile <= W && W % 16 == 0 && H % 16 == 0) {
+        const int i = threadIdx.x >> 2, j0 = (threadIdx.x & 3) * 16;   // tile row i, columns j0..j0+15
+        const size_t o = (size_t)(r0 + i) * W + c0 + j0;
+        constexpr int N = 16 / (int)sizeof(T);
+        float acc[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+        for (int slot = 0; slot < prm.nd; ++slot) {
+            float pv[16];
+            if (prm.dir_of_slot[slot] < 2) {
+                const float* P = prm.planes + slot * E + bc * HW + o;
+#pragma unroll
+                for (int e = 0; e < 16; e += 4) {
+                    const float4 v = *reinterpret_cast<const float4*>(P + e);
+                    pv[e] = v.x; pv[e + 1] = v.y; pv[e + 2] = v.z; pv[e + 3] = v.w;
+                }
+            } else {
+                // this thread reads line c0 + i (rows r0+j0 ..) and takes
+                // back row r0 + i, columns c0+j0 .. from the tile
+                const float* P = prm.planes + slot * E + bc * HW + (size_t)(c0 + i) * H + r0 + j0;
+#pragma unroll
+                for (int e = 0; e < 16; e += 4) {
+                    const float4 v = *reinterpret_cast<const float4*>(P + e);
+                    tile[i][j0 + e] = v.x; tile[i][j0 + e + 1] = v.y;
+                    tile[i][j0 + e + 2] = v.z; tile[i][j0 + e + 3] = v.w;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < 16; ++e) pv[e] = tile[j0 + e][i];
+                __syncthreads();
+            }
+            const T* us = gu + slot * E + o;
+#pragma unroll
+            for (int e = 0; e < 16; e += N) {
+                float f[N];
+                unpack(*reinterpret_cast<const uint4*>(us + e), f);
+#pragma unroll
+                for (int q = 0; q < N; ++q) acc[e + q] = fmaf(f[q], pv[e + q], acc[e + q]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; e += N) {
+            float f[N];
+#pragma unroll
+            for (int q = 0; q < N; ++q) f[q] = acc[e + q];
+            store16_nt(gy + o + e, f);
+        }
+        return;
+    }
+
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    float acc[kTile / 4];
+#pragma unroll
+    for (int s = 0; s < kTile / 4; ++s) acc[s] = 0.0f;
+    for (int slot = 0; slot < prm.nd; ++slot) {
+        const float* P = prm.planes + slot * E + bc * HW;
+        const T* us = gu + slot * E;
+        if (prm.dir_of_slot[slot] < 2) {
+#pragma unroll
+            for (int s = 0; s < kTile / 4; ++s) {
+                const int r = r0 + ty + 4 * s, q = c0 + tx;
+                if (r < H && q < W) acc[s] = fmaf(to_f32(us[(size_t)r * W + q]), P[(size_t)r * W + q], acc[s]);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < kTile / 4; ++s) {
+                const int q = c0 + ty + 4 * s, r = r0 + tx;
+                tile[ty + 4 * s][tx] = (q < W && r < H) ? P[(size_t)q * H + r] : 0.0f;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < kTile / 4; ++s) {
+                const int r = r0 + ty + 4 * s, q = c0 + tx;
+                if (r < H && q < W) acc[s] = fmaf(to_f32(us[(size_t)r * W + q]), tile[tx][ty + 4 * s], acc[s]);
+            }
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < kTile / 4; ++s) {
+        const int r = r0 + ty + 4 * s, q = c0 + tx;
+        if (r < H && q < W) __builtin_nontemporal_store(from_f32(acc[s], (T*)nullptr), gy + (size_t)r * W + q);
+    }
+}
+
 }  // namespace
 }  // namespace gspn
 
@@ -482,6 +590,14 @@ void launch_line_scan(const LineParams& p, hipStream_t stream) {
     else if (m <= 128) hipLaunchKernelGGL((line_scan_kernel<T, 2>), grid, dim3(256), 0, stream, p);
     else if (m <= 256) hipLaunchKernelGGL((line_scan_kernel<T, 4>), grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((line_scan_kernel<T, 8>), grid, dim3(256), 0, stream, p);
+}
+
+template <typename T>
+void launch_merge_dirs(MergeParams q, hipStream_t stream) {
+    q.tiles_r = (q.H + kTile - 1) / kTile;
+    q.tiles_c = (q.W + kTile - 1) / kTile;
+    hipLaunchKernelGGL((merge_dirs_kernel<T>), dim3((unsigned)((size_t)q.B * q.C * q.tiles_r * q.tiles_c)),
+                       dim3(256), 0, stream, q);
 }
 
 template <typename T, int NP>

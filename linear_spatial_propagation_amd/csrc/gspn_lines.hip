@@ -29,6 +29,9 @@ hipError_t launch_lines_t(const ScanArgs& a, const LinesWorkspace& ws, hipStream
     p.xT = ws.xT; p.lamT = ws.lamT; p.wT = ws.wT;
     p.planes = ws.planes;
     p.sink = ws.sink;
+    const size_t E = (size_t)a.B * a.C * H * W;
+    p.lam_ds = a.lam_dir ? E : 0;
+    p.lamT_ds = a.lam_dir ? E : 0;
     p.B = a.B; p.C = a.C; p.H = H; p.W = W; p.Cw = Cw; p.cpw = a.cpw; p.groups = a.groups;
     int ncol = 0;
     p.nd = enabled_slots(a.dirs, p.dir_of_slot, p.col_index, &ncol);
@@ -37,7 +40,15 @@ hipError_t launch_lines_t(const ScanArgs& a, const LinesWorkspace& ws, hipStream
     if (ncol > 0) {
         const size_t planes_xl = (size_t)a.B * a.C;
         launch_transpose(static_cast<const T*>(a.x), static_cast<T*>(ws.xT), planes_xl, H, W, stream);
-        launch_transpose(static_cast<const T*>(a.lam), static_cast<T*>(ws.lamT), planes_xl, H, W, stream);
+        if (a.lam_dir) {
+            for (int s = 0; s < p.nd; ++s) {
+                if (p.dir_of_slot[s] < 2) continue;
+                launch_transpose(static_cast<const T*>(a.lam) + (size_t)s * E,
+                                 static_cast<T*>(ws.lamT) + (size_t)p.col_index[s] * E, planes_xl, H, W, stream);
+            }
+        } else {
+            launch_transpose(static_cast<const T*>(a.lam), static_cast<T*>(ws.lamT), planes_xl, H, W, stream);
+        }
         const size_t wslab = (size_t)a.B * Cw * 3;
         for (int s = 0; s < p.nd; ++s) {
             if (p.dir_of_slot[s] < 2) continue;
@@ -53,7 +64,8 @@ hipError_t launch_lines_t(const ScanArgs& a, const LinesWorkspace& ws, hipStream
     q.planes = ws.planes;
     q.B = a.B; q.C = a.C; q.H = H; q.W = W; q.nd = p.nd;
     for (int s = 0; s < 4; ++s) q.dir_of_slot[s] = p.dir_of_slot[s];
-    launch_merge<T, 1>(q, stream);
+    if (a.u_dir) launch_merge_dirs<T>(q, stream);
+    else launch_merge<T, 1>(q, stream);
     return hipGetLastError();
 }
 
@@ -79,7 +91,7 @@ size_t lines_workspace_bytes(const ScanArgs& a) {
         if ((a.dirs >> d) & 1u) { ++nd; if (d >= 2) ++ncol; }
     const size_t Ew = (size_t)a.B * (a.C / a.cpw) * 3 * a.H * a.W;
     size_t bytes = (size_t)nd * E * sizeof(float) + kSinkBytes;
-    if (ncol) bytes += 2 * E * es + (size_t)ncol * Ew * es;
+    if (ncol) bytes += E * es + (a.lam_dir ? ncol : 1) * E * es + (size_t)ncol * Ew * es;
     return bytes;
 }
 
@@ -98,7 +110,7 @@ hipError_t launch_lines(const ScanArgs& a, void* workspace, hipStream_t stream) 
     ws.xT = ncol ? base : nullptr;
     base += ncol ? E * es : 0;
     ws.lamT = ncol ? base : nullptr;
-    base += ncol ? E * es : 0;
+    base += ncol ? (a.lam_dir ? ncol : 1) * E * es : 0;
     ws.wT = ncol ? base : nullptr;
     return a.bf16 ? launch_lines_t<uint16_t>(a, ws, stream) : launch_lines_t<float>(a, ws, stream);
 }

@@ -393,6 +393,8 @@ hipError_t launch_lines_bwd_t(const GradArgs& g, void* workspace, hipStream_t st
     p.xT = xT; p.lamT = lamT; p.wT = wT;
     p.planes = planes;
     p.sink = sink;
+    p.lam_ds = 0;   // the backward takes lambda and u shared by all directions
+    p.lamT_ds = 0;
     p.B = a.B; p.C = a.C; p.H = H; p.W = W; p.Cw = Cw; p.cpw = a.cpw; p.groups = a.groups;
     int ncol = 0;
     p.nd = enabled_slots(a.dirs, p.dir_of_slot, p.col_index, &ncol);

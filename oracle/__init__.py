@@ -96,6 +96,28 @@ def scan_fwd(x, w, lam, u, *, dirs: int = 15, groups: int = 1, cpw: int = 1,
     return y
 
 
+def scan_fwd_dirs(x, w, lam, u, *, dirs: int = 15, groups: int = 1, cpw: int = 1,
+                  nthreads: int = 0) -> np.ndarray:
+    """Per-direction variant: y = sum_d u_d * h_d, h_d driven by lam_d * x.
+
+    lam and u are [B][C][H][W] (shared) or [popcount(dirs)][B][C][H][W].
+    Written as the sum of single-direction calls of the oracle above, which
+    computes u_d * h_d for one direction exactly as the definition states.
+    """
+    x, w, lam, u = (_f64c(a) for a in (x, w, lam, u))
+    y = np.zeros_like(x)
+    slab = 0
+    for d in range(4):
+        if not (dirs >> d) & 1:
+            continue
+        lam_d = lam[slab] if lam.ndim == 5 else lam
+        u_d = u[slab] if u.ndim == 5 else u
+        y += scan_fwd(x, w[slab:slab + 1], lam_d, u_d, dirs=1 << d, groups=groups, cpw=cpw,
+                      nthreads=nthreads)
+        slab += 1
+    return y
+
+
 def scan_bwd(x, w, lam, u, gy, *, dirs: int = 15, groups: int = 1, cpw: int = 1,
              nthreads: int = 0, lib=None):
     """Gradients (gx, gw, glam, gu) in fp64 of L with dL/dy = gy.

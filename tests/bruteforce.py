@@ -85,7 +85,11 @@ def scan_tb_dense(xl: np.ndarray, taps: np.ndarray, groups: int, check: bool = T
 
 def bruteforce_fwd(x, w, lam, u, *, dirs: int = 15, groups: int = 1, cpw: int = 1,
                    check: bool = True) -> np.ndarray:
-    """y[B][C][H][W] by the dense closed form.  Same tensor layouts as the oracle."""
+    """y[B][C][H][W] by the dense closed form.  Same tensor layouts as the oracle.
+
+    lam and u may also carry a leading direction axis ([ndir][B][C][H][W]):
+    then direction d is driven by its own lam_d and y = sum_d u_d h_d.
+    """
     x, w, lam, u = (np.asarray(a, dtype=np.float64) for a in (x, w, lam, u))
     B, C, H, W = x.shape
     y = np.zeros_like(x)
@@ -97,9 +101,11 @@ def bruteforce_fwd(x, w, lam, u, *, dirs: int = 15, groups: int = 1, cpw: int = 
                 if not (dirs >> d) & 1:
                     continue
                 taps = w[slab, b, c // cpw]          # [3][H][W]
+                lam_bc = lam[slab, b, c] if lam.ndim == 5 else lam[b, c]
+                gate = u[slab, b, c] if u.ndim == 5 else np.ones((H, W))
                 slab += 1
-                xl = _to_tb(lam[b, c] * x[b, c], d)
+                xl = _to_tb(lam_bc * x[b, c], d)
                 h = scan_tb_dense(xl, _to_tb(taps, d), groups, check)
-                acc += _from_tb(h, d)
-            y[b, c] = u[b, c] * acc
+                acc += gate * _from_tb(h, d)
+            y[b, c] = acc if u.ndim == 5 else u[b, c] * acc
     return y

@@ -139,3 +139,35 @@ def test_bwd_supported(lib):
     assert _lib.bwd_supported(1, 8, 130, 64) == -10     # 130 is not a multiple of K = 4
     assert _lib.bwd_supported(1, 8, 513, 64) == -10
     assert _lib.bwd_supported(1, 8, 32, 32, groups=5) == -4
+
+
+def call_ex(**kw):
+    args = dict(x=FAKE, w=FAKE + (1 << 32), lam=FAKE + (2 << 32), u=FAKE + (3 << 32), y=FAKE + (4 << 32),
+                B=2, C=8, H=16, W=16, dirs=15, groups=1, ch_per_weight=1, flags=1, dtype=1)
+    args.update(kw)
+    return _lib.scan_fwd_ex_ptr(args["x"], args["w"], args["lam"], args["u"], args["y"], args["B"],
+                                args["C"], args["H"], args["W"], dirs=args["dirs"], groups=args["groups"],
+                                ch_per_weight=args["ch_per_weight"], flags=args["flags"],
+                                dtype=args["dtype"])
+
+
+NBYTES = 2 * 8 * 16 * 16 * 2   # one bf16 [B][C][H][W] slab of call_ex's default shape
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=4), -11), (dict(flags=0xFF), -11),
+    (dict(B=0), -2), (dict(dirs=0), -3), (dict(groups=3), -4), (dict(ch_per_weight=3), -5),
+    (dict(dtype=2), -6), (dict(lam=0), -1), (dict(u=0), -1), (dict(x=FAKE + 4), -7),
+    (dict(y=FAKE + (2 << 32) + NBYTES), -8),             # y inside the second lambda slab
+    (dict(flags=2, y=FAKE + (3 << 32) + 3 * NBYTES), -8), # y inside the last gate slab
+    (dict(H=130), -10), (dict(flags=3, W=600), -10),
+])
+def test_variant_invalid_arguments_rejected_on_host(lib, kw, code):
+    assert call_ex(**kw) == code
+
+
+def test_python_variant_wrapper_rejects_bad_shapes():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 2, 4, 4)
+    with pytest.raises(ValueError):
+        gspn.scan_fwd_dirs(x, torch.zeros(4, 1, 2, 3, 4, 4), torch.zeros(3, 1, 2, 4, 4), x)
