@@ -30,6 +30,10 @@ consumes, gx, glam, gu once and the whole tap-gradient tensor once:
     + s * ndir * B * Cw * 3 * H * W.
 Its roofline object covers the whole call (all of its launches).
 
+With --batched K (grids up to 64 x 64) a step is one gspn_scan_fwd_batched
+call over K copies of the workload (own buffers each), and the same K
+problems are also timed as K separate gspn_scan_fwd calls for comparison.
+
 With --variant dirs a step is one call of gspn_scan_fwd_ex with lambda and
 u per direction (y = sum_d u_d * h_d); the algorithmic bytes count the four
 lambda and four u slabs once:
@@ -270,6 +274,8 @@ def main():
                     help="time the forward (default) or the backward")
     ap.add_argument("--variant", choices=("none", "dirs"), default="none",
                     help="dirs: the forward with per-direction lambda and u (gspn_scan_fwd_ex)")
+    ap.add_argument("--batched", type=int, default=1,
+                    help="K > 1: K copies of the workload in one batched launch (gspn_scan_fwd_batched)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for counter calibration)")
@@ -309,6 +315,7 @@ def main():
 
     bwd = args.pass_ == "bwd"
     dirs_variant = args.variant == "dirs" and not bwd
+    batched = args.batched if not bwd and not dirs_variant else 1
     base = [up(a) for a in (wl.x_store, wl.w_store, wl.lam_store, wl.u_store)]
     if dirs_variant:
         # per-direction lambda and u: U(0, 1), seeded, in the workload's dtype
@@ -327,17 +334,47 @@ def main():
     else:
         nbytes = algorithmic_bytes(B, C, H, W, 15, wl.groups, wl.cpw, wl.dtype)
         outs_like = [base[0]]
-    footprint = sum(t.numel() * t.element_size() for t in base + outs_like)
+    if batched > 1:
+        nbytes *= batched
+    footprint = sum(t.numel() * t.element_size() for t in base + outs_like) * batched
     R = max(1, -(-512 * 1024 * 1024 // footprint))
     sets = []
     for r in range(R):
         ins = [t.clone() for t in base] if r else base
         sets.append((ins, [torch.empty_like(t) for t in outs_like]))
     stream = torch.cuda.current_stream(dev)
+    if batched > 1:
+        # K problems per buffer set, each with its own tensors
+        bsets = []
+        for r in range(R):
+            bsets.append([dict(x=t[0].clone(), w_raw=t[1].clone(), lam=t[2].clone(), u=t[3].clone(),
+                               out=torch.empty_like(base[0]), dirs=15, groups=wl.groups,
+                               ch_per_weight=wl.cpw)
+                          for t in [sets[r][0]] * batched])
+        # descriptor arrays built once: a step is one call of the C ABI
+        from linear_spatial_propagation_amd import _lib
+        dtc = _lib.GSPN_BF16 if wl.dtype == "bf16" else _lib.GSPN_F32
+        barrays = []
+        for probs in bsets:
+            arr = (_lib.Problem * batched)(*[
+                _lib.Problem(pr["x"].data_ptr(), pr["w_raw"].data_ptr(), pr["lam"].data_ptr(),
+                             pr["u"].data_ptr(), pr["out"].data_ptr(), B, C, H, W, 15, wl.groups, wl.cpw)
+                for pr in probs])
+            barrays.append(arr)
+        batched_fn = _lib.load().gspn_scan_fwd_batched
+        stream_handle = stream.cuda_stream
+
+    def step_separate(i):
+        for pr in bsets[i % R]:
+            gspn.scan_fwd(pr["x"], pr["w_raw"], pr["lam"], pr["u"], dirs=15, groups=wl.groups,
+                          ch_per_weight=wl.cpw, out=pr["out"])
+
 
     def step(i):
         ins, outs = sets[i % R]
-        if bwd:
+        if batched > 1:
+            _lib.check(batched_fn(barrays[i % R], batched, dtc, stream_handle))
+        elif bwd:
             gspn.scan_bwd(*ins, dirs=15, groups=wl.groups, ch_per_weight=wl.cpw, out=outs)
         elif dirs_variant:
             gspn.scan_fwd_dirs(*ins, dirs=15, groups=wl.groups, ch_per_weight=wl.cpw, out=outs[0])
@@ -375,6 +412,17 @@ def main():
         b.record(stream)
     torch.cuda.synchronize(dev)
     hot = np.array([a.elapsed_time(b) for a, b in hot_ev]) * 1e-3
+
+    separate_us = None
+    if batched > 1:
+        sep_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(min(args.steps, 100))]
+        for i, (a, b) in enumerate(sep_ev):
+            a.record(stream)
+            step_separate(i)
+            b.record(stream)
+        torch.cuda.synchronize(dev)
+        separate_us = float(np.median([a.elapsed_time(b) for a, b in sep_ev])) * 1e3
 
     if args.copy_calibration:
         src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
@@ -414,7 +462,7 @@ def main():
             "seed": cfgd["seed"],
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "elements_per_s": round(E * args.steps / elapsed, 1),
+        "elements_per_s": round(E * batched * args.steps / elapsed, 1),
         "launch_us": {"mean": round(avg_launch * 1e6, 3), "p10": round(float(np.percentile(per, 10)) * 1e6, 3),
                       "median": round(float(np.median(per)) * 1e6, 3),
                       "p90": round(float(np.percentile(per, 90)) * 1e6, 3)},
@@ -425,11 +473,18 @@ def main():
     }
     if dirs_variant:
         out["roofline"]["kernel"] = "gspn_scan_fwd_ex, all launches of one call"
+    if batched > 1:
+        out["metric"] = METRIC + f" ({batched} problems per batched launch)"
+        out["config"]["batched_problems"] = batched
+        out["config"]["path"] = "fused, batched"
+        out["roofline"]["kernel"] = "fused_scan_batched_kernel"
+        out["roofline"]["traffic"] = None
+        out["separate_launches_us"] = round(separate_us, 3)
     if bwd:
         # 64 x 64 grids and smaller: one fused kernel per call
         out["roofline"]["kernel"] = ("fused_bwd_kernel" if max(H, W) <= 64
                                      else "gspn_scan_bwd, all launches of one call")
-    if not args.no_cpu and not dirs_variant:
+    if not args.no_cpu and not dirs_variant and batched == 1:
         out["cpu_baseline"] = cpu_baseline(args.config, backward=bwd)
     print(json.dumps(out), flush=True)
 

@@ -174,6 +174,33 @@ int gspn_scan_fwd_ex(const void *x, const void *w_raw, const void *lam, const vo
                      int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
                      int32_t ch_per_weight, uint32_t flags, int32_t dtype, hipStream_t stream);
 
+/*
+ * Several independent forward problems in one launch, for workloads too
+ * small to occupy the GPU alone (GSPN-2 author response, "SM Utilization
+ * for Small Workloads": micro-batching small launches).  Each problem is
+ * exactly one gspn_scan_fwd call (its own tensors, sizes, dirs, groups and
+ * ch_per_weight); all share `dtype` and `stream`.
+ *   problems : host array of `count` descriptors (1 <= count <=
+ *              GSPN_MAX_BATCH), read during the call only
+ * Every problem must take the fused path (H <= 64 and W <= 64), else
+ * GSPN_ERR_PATH; count outside [1, GSPN_MAX_BATCH] gives GSPN_ERR_SHAPE.
+ * Each problem is validated as gspn_scan_fwd validates its arguments, and
+ * no problem's y may overlap any problem's input or another problem's y
+ * (GSPN_ERR_ALIAS).  On any error nothing is launched.  Results equal those
+ * of separate gspn_scan_fwd calls (the same kernel code runs every problem).
+ */
+#define GSPN_MAX_BATCH 32
+
+typedef struct {
+    const void *x, *w_raw, *lam, *u; /* inputs, layouts as in gspn_scan_fwd */
+    void *y;                         /* output */
+    int64_t B, C, H, W;
+    uint32_t dirs;
+    int32_t groups, ch_per_weight;
+} gspn_problem;
+
+int gspn_scan_fwd_batched(const gspn_problem *problems, int32_t count, int32_t dtype, hipStream_t stream);
+
 /* The path gspn_scan_fwd would take for these sizes (GSPN_PATH_FUSED or
  * GSPN_PATH_GENERAL), or a negative error code for invalid sizes. */
 int gspn_select_path(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,

@@ -3,6 +3,7 @@
     y = scan_fwd(x, w_raw, lam, u, dirs=15, groups=1, ch_per_weight=1)
     gx, gw_raw, glam, gu = scan_bwd(x, w_raw, lam, u, gy, dirs=15, groups=1, ch_per_weight=1)
     y = scan_fwd_dirs(x, w_raw, lam_d, u_d, ...)   # per-direction gains / gates
+    ys = scan_fwd_batched([dict(x=..., w_raw=..., lam=..., u=...), ...])   # one launch
 
 computes the 4-direction line recurrence of the Generalized Spatial
 Propagation Network with hand-written HIP kernels (libgspn.so, C ABI in
@@ -19,7 +20,7 @@ from . import _lib
 from ._lib import (DIR_ALL, DIR_BT, DIR_LR, DIR_RL, DIR_TB, PATH_AUTO, PATH_FUSED, PATH_GENERAL,
                    GspnError, load, select_path)
 
-__all__ = ["scan_fwd", "scan_bwd", "scan_fwd_dirs", "select_path", "load", "GspnError", "DIR_TB", "DIR_BT", "DIR_LR", "DIR_RL",
+__all__ = ["scan_fwd", "scan_bwd", "scan_fwd_dirs", "scan_fwd_batched", "select_path", "load", "GspnError", "DIR_TB", "DIR_BT", "DIR_LR", "DIR_RL",
            "DIR_ALL", "PATH_AUTO", "PATH_FUSED", "PATH_GENERAL"]
 
 
@@ -129,6 +130,40 @@ def scan_fwd_dirs(x, w_raw, lam, u, *, dirs: int = DIR_ALL, groups: int = 1, ch_
                                   stream=stream)
     _lib.check(rc)
     return out
+
+
+def scan_fwd_batched(problems):
+    """Several independent forward problems (each H, W <= 64) in one launch.
+
+    problems: sequence of dicts with keys x, w_raw, lam, u and optionally
+    dirs, groups, ch_per_weight, out.  All tensors share one dtype and
+    device.  Returns the list of y tensors.
+    """
+    import torch
+    if not problems:
+        raise ValueError("no problems")
+    structs, outs, dev, dt = [], [], None, None
+    for pr in problems:
+        dirs = pr.get("dirs", DIR_ALL)
+        cpw = pr.get("ch_per_weight", 1)
+        d, (B, C, H, W) = _check_inputs({"x": pr["x"], "w_raw": pr["w_raw"], "lam": pr["lam"], "u": pr["u"]},
+                                        dirs, cpw)
+        if dev is None:
+            dev, dt = d, pr["x"].dtype
+        elif d != dev or pr["x"].dtype != dt:
+            raise ValueError("all problems must share one device and dtype")
+        y = pr.get("out")
+        if y is None:
+            y = torch.empty_like(pr["x"])
+        outs.append(y)
+        structs.append(_lib.Problem(pr["x"].data_ptr(), pr["w_raw"].data_ptr(), pr["lam"].data_ptr(),
+                                    pr["u"].data_ptr(), y.data_ptr(), B, C, H, W, dirs,
+                                    pr.get("groups", 1), cpw))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = _lib.scan_fwd_batched_ptr(structs, dtype=_dtype_code(problems[0]["x"]), stream=stream)
+    _lib.check(rc)
+    return outs
 
 
 def scan_fwd(x, w_raw, lam, u, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1,

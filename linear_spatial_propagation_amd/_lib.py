@@ -21,8 +21,18 @@ PATH_GENERAL = 2
 DIR_TB, DIR_BT, DIR_LR, DIR_RL, DIR_ALL = 1, 2, 4, 8, 15
 
 LAM_PER_DIR, U_PER_DIR = 1, 2
+MAX_BATCH = 32
 
-EXPORTED = ("gspn_scan_fwd", "gspn_scan_fwd_path", "gspn_scan_fwd_ex", "gspn_select_path", "gspn_scan_bwd",
+
+class Problem(ctypes.Structure):
+    """gspn_problem of include/gspn.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("w_raw", ctypes.c_void_p), ("lam", ctypes.c_void_p),
+                ("u", ctypes.c_void_p), ("y", ctypes.c_void_p), ("B", ctypes.c_int64),
+                ("C", ctypes.c_int64), ("H", ctypes.c_int64), ("W", ctypes.c_int64),
+                ("dirs", ctypes.c_uint32), ("groups", ctypes.c_int32), ("ch_per_weight", ctypes.c_int32)]
+
+EXPORTED = ("gspn_scan_fwd", "gspn_scan_fwd_path", "gspn_scan_fwd_ex", "gspn_scan_fwd_batched",
+            "gspn_select_path", "gspn_scan_bwd",
             "gspn_scan_bwd_path", "gspn_bwd_supported", "gspn_status_string", "gspn_last_error", "gspn_version")
 
 _lock = threading.Lock()
@@ -53,6 +63,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.gspn_scan_fwd_path.restype = ctypes.c_int
         lib.gspn_scan_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, u32, i32, i32, u32, i32, vp]
         lib.gspn_scan_fwd_ex.restype = ctypes.c_int
+        lib.gspn_scan_fwd_batched.argtypes = [ctypes.POINTER(Problem), i32, i32, vp]
+        lib.gspn_scan_fwd_batched.restype = ctypes.c_int
         lib.gspn_select_path.argtypes = [i64, i64, i64, i64, u32, i32, i32, i32]
         lib.gspn_select_path.restype = ctypes.c_int
         lib.gspn_scan_bwd.argtypes = [vp] * 9 + [i64, i64, i64, i64, u32, i32, i32, i32, vp]
@@ -97,6 +109,12 @@ def scan_fwd_ex_ptr(x: int, w: int, lam: int, u: int, y: int, B: int, C: int, H:
     """Raw call of the per-direction variant on device pointers; returns the status code."""
     return load().gspn_scan_fwd_ex(x, w, lam, u, y, B, C, H, W, dirs, groups, ch_per_weight, flags,
                                    dtype, stream)
+
+
+def scan_fwd_batched_ptr(problems, dtype: int = GSPN_BF16, stream: int = 0) -> int:
+    """Raw batched call: `problems` is a sequence of Problem; returns the status code."""
+    arr = (Problem * max(1, len(problems)))(*problems)
+    return load().gspn_scan_fwd_batched(arr, len(problems), dtype, stream)
 
 
 def scan_bwd_ptr(x: int, w: int, lam: int, u: int, gy: int, gx: int, gw: int, glam: int, gu: int,

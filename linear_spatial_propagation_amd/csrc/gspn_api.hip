@@ -157,6 +157,50 @@ int gspn_scan_fwd_ex(const void* x, const void* w_raw, const void* lam, const vo
                          GSPN_PATH_AUTO, stream);
 }
 
+int gspn_scan_fwd_batched(const gspn_problem* problems, int32_t count, int32_t dtype, hipStream_t stream) {
+    g_last_error[0] = '\0';
+    if (!problems) return GSPN_ERR_NULL;
+    if (count < 1 || count > GSPN_MAX_BATCH) return GSPN_ERR_SHAPE;
+    if (dtype != GSPN_F32 && dtype != GSPN_BF16) return GSPN_ERR_DTYPE;
+    const size_t es = dtype == GSPN_BF16 ? 2 : 4;
+    gspn::ScanArgs args[GSPN_MAX_BATCH];
+    for (int i = 0; i < count; ++i) {
+        const gspn_problem& q = problems[i];
+        const int rc = check_sizes(q.B, q.C, q.H, q.W, q.dirs, q.groups, q.ch_per_weight, dtype);
+        if (rc) return rc;
+        if (!q.x || !q.w_raw || !q.lam || !q.u || !q.y) return GSPN_ERR_NULL;
+        const void* ptrs[5] = {q.x, q.w_raw, q.lam, q.u, q.y};
+        for (const void* v : ptrs)
+            if ((uintptr_t)v & 15u) return GSPN_ERR_ALIGN;
+        if (auto_path(q.H, q.W) != GSPN_PATH_FUSED) {
+            set_error_text("every problem of a batch must take the fused path (H, W <= 64)");
+            return GSPN_ERR_PATH;
+        }
+        gspn::ScanArgs& a = args[i];
+        a.x = q.x; a.w = q.w_raw; a.lam = q.lam; a.u = q.u; a.y = q.y;
+        a.B = (int)q.B; a.C = (int)q.C; a.H = (int)q.H; a.W = (int)q.W;
+        a.dirs = q.dirs; a.groups = q.groups; a.cpw = q.ch_per_weight; a.bf16 = dtype == GSPN_BF16;
+        a.lam_dir = 0; a.u_dir = 0;
+    }
+    // no output overlaps an input of any problem or another output
+    for (int i = 0; i < count; ++i) {
+        const gspn_problem& q = problems[i];
+        const size_t ny = (size_t)q.B * q.C * q.H * q.W * es;
+        for (int j = 0; j < count; ++j) {
+            const gspn_problem& r = problems[j];
+            const size_t n = (size_t)r.B * r.C * r.H * r.W * es;
+            const size_t nw = (size_t)popcount4(r.dirs) * r.B * (r.C / r.ch_per_weight) * 3 * r.H * r.W * es;
+            if (overlaps(q.y, ny, r.x, n) || overlaps(q.y, ny, r.lam, n) || overlaps(q.y, ny, r.u, n) ||
+                overlaps(q.y, ny, r.w_raw, nw))
+                return GSPN_ERR_ALIAS;
+            if (j != i && overlaps(q.y, ny, r.y, n)) return GSPN_ERR_ALIAS;
+        }
+    }
+    const hipError_t e = gspn::launch_fused_batched(args, count, stream);
+    if (e != hipSuccess) { set_error("batched fused kernel launch", e); return GSPN_ERR_HIP; }
+    return GSPN_OK;
+}
+
 int gspn_scan_fwd(const void* x, const void* w_raw, const void* lam, const void* u, void* y,
                   int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
                   int32_t ch_per_weight, int32_t dtype, hipStream_t stream) {

@@ -45,6 +45,7 @@ constexpr int kPitch = kS + 4;       // LDS row pitch (floats): rows 16-byte ali
                                      // and 4-wide column accesses are conflict-free
 constexpr int kPlane = kS * kPitch;  // floats per LDS plane
 constexpr int kThreads = 256;
+constexpr int kMaxBatch = 32;        // problems per batched launch (kernel-argument space)
 
 struct FusedParams {
     const void* x;
@@ -435,10 +436,10 @@ __device__ __forceinline__ void stage_taps_scalar(float* Sd, const TapSrc<T>& ws
 }
 
 // ---------------------------------------------------------------- kernel
-// VEC: every row is a whole number of 16-byte vectors (W % N == 0).
+// The work of workgroup `wg` of one problem.  VEC: every row is a whole
+// number of 16-byte vectors (W % N == 0).
 template <typename T, bool VEC>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
-void fused_scan_kernel(FusedParams prm) {
+__device__ __forceinline__ void fused_scan_body(const FusedParams& prm, const int wg) {
     constexpr int N = Vec<T>::N;                     // elements per 16-byte access
     constexpr int kMaxIt = kS * kS / (kThreads * N); // merge/staging iterations
     constexpr int kChunk = 16;
@@ -458,7 +459,6 @@ void fused_scan_kernel(FusedParams prm) {
     constexpr bool vec = VEC;
 
     // ---- which (b, k, chunk) this workgroup owns
-    const int wg = blockIdx.x;
     const int chunk = wg % prm.nchunk;
     const int bk = wg / prm.nchunk;
     const int k = bk % Cw;
@@ -717,21 +717,85 @@ void fused_scan_kernel(FusedParams prm) {
     }
 }
 
-}  // namespace
+template <typename T, bool VEC>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void fused_scan_kernel(FusedParams prm) {
+    fused_scan_body<T, VEC>(prm, blockIdx.x);
+}
 
-hipError_t launch_fused(const ScanArgs& a, hipStream_t stream) {
+// Several independent problems in one launch: problem i owns workgroups
+// [wg_begin[i], wg_begin[i+1]).  Small problems then share the GPU instead
+// of each leaving most of it idle.
+struct FusedBatch {
+    FusedParams p[kMaxBatch];
+    int wg_begin[kMaxBatch + 1];
+    int count;
+};
+
+template <typename T, bool VEC>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void fused_scan_batched_kernel(FusedBatch bat) {
+    const int wg = blockIdx.x;
+    int i = 0;
+    while (i + 1 < bat.count && wg >= bat.wg_begin[i + 1]) ++i;   // uniform
+    fused_scan_body<T, VEC>(bat.p[i], wg - bat.wg_begin[i]);
+}
+
+// Channel chunks per weight set: split a set's channels over several
+// workgroups only when there are too few (b, k) pairs in the launch to
+// occupy the GPU (two workgroups per CU).
+void set_chunks(FusedParams& p, long sets_in_launch) {
+    const long want = 512;
+    int nchunk = 1;
+    if (sets_in_launch < want) nchunk = (int)std::min<long>(p.cpw, (want + sets_in_launch - 1) / sets_in_launch);
+    p.chunk_len = (p.cpw + nchunk - 1) / nchunk;
+    p.nchunk = (p.cpw + p.chunk_len - 1) / p.chunk_len;
+}
+
+FusedParams fused_params(const ScanArgs& a) {
     FusedParams p;
     p.x = a.x; p.w = a.w; p.lam = a.lam; p.u = a.u; p.y = a.y;
     p.B = a.B; p.C = a.C; p.H = a.H; p.W = a.W;
     p.cpw = a.cpw; p.Cw = a.C / a.cpw; p.groups = a.groups; p.dirs = a.dirs;
-    // Split a weight set's channels over several workgroups only when there
-    // are too few (b, k) pairs to occupy the GPU (two workgroups per CU).
+    return p;
+}
+
+}  // namespace
+
+hipError_t launch_fused_batched(const ScanArgs* probs, int count, hipStream_t stream) {
+    if (count < 1 || count > kMaxBatch) return hipErrorInvalidValue;
+    FusedBatch bat;
+    long sets = 0;
+    bool vec = true;
+    for (int i = 0; i < count; ++i) {
+        sets += (long)probs[i].B * (probs[i].C / probs[i].cpw);
+        vec = vec && probs[i].W % (probs[0].bf16 ? Vec<uint16_t>::N : Vec<float>::N) == 0;
+    }
+    int wg = 0;
+    for (int i = 0; i < count; ++i) {
+        bat.p[i] = fused_params(probs[i]);
+        set_chunks(bat.p[i], sets);
+        bat.wg_begin[i] = wg;
+        wg += bat.p[i].B * bat.p[i].Cw * bat.p[i].nchunk;
+    }
+    for (int i = count; i <= kMaxBatch; ++i) bat.wg_begin[i] = wg;
+    for (int i = count; i < kMaxBatch; ++i) bat.p[i] = bat.p[0];
+    bat.count = count;
+    const unsigned grid = (unsigned)wg;
+    if (probs[0].bf16) {
+        if (vec) hipLaunchKernelGGL((fused_scan_batched_kernel<uint16_t, true>), dim3(grid), dim3(kThreads), 0, stream, bat);
+        else hipLaunchKernelGGL((fused_scan_batched_kernel<uint16_t, false>), dim3(grid), dim3(kThreads), 0, stream, bat);
+    } else {
+        if (vec) hipLaunchKernelGGL((fused_scan_batched_kernel<float, true>), dim3(grid), dim3(kThreads), 0, stream, bat);
+        else hipLaunchKernelGGL((fused_scan_batched_kernel<float, false>), dim3(grid), dim3(kThreads), 0, stream, bat);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fused(const ScanArgs& a, hipStream_t stream) {
+    FusedParams p = fused_params(a);
     const long sets = (long)a.B * p.Cw;
-    const long want = 512;
-    int nchunk = 1;
-    if (sets < want) nchunk = (int)std::min<long>(a.cpw, (want + sets - 1) / sets);
-    p.chunk_len = (a.cpw + nchunk - 1) / nchunk;
-    p.nchunk = (a.cpw + p.chunk_len - 1) / p.chunk_len;
+    set_chunks(p, sets);
     const unsigned grid = (unsigned)(sets * p.nchunk);
     const bool vec = a.W % (a.bf16 ? Vec<uint16_t>::N : Vec<float>::N) == 0;
     if (a.bf16) {

@@ -25,6 +25,8 @@ struct ScanArgs {
 // Fused 4-direction kernel: H <= 64 and W <= 64.
 constexpr int kFusedMaxSide = 64;
 hipError_t launch_fused(const ScanArgs& a, hipStream_t stream);
+// Up to 32 validated fused-path problems of one dtype in one launch.
+hipError_t launch_fused_batched(const ScanArgs* probs, int count, hipStream_t stream);
 
 // Line path: H, W <= kLinesMaxSide with both sides multiples of K (the
 // positions per lane, lines_positions_per_lane).  Workspace layout, in

@@ -171,3 +171,26 @@ def test_python_variant_wrapper_rejects_bad_shapes():
     x = torch.zeros(1, 2, 4, 4)
     with pytest.raises(ValueError):
         gspn.scan_fwd_dirs(x, torch.zeros(4, 1, 2, 3, 4, 4), torch.zeros(3, 1, 2, 4, 4), x)
+
+
+def prob(i=0, **kw):
+    base = FAKE + (i << 36)
+    d = dict(x=base, w_raw=base + (1 << 32), lam=base + (2 << 32), u=base + (3 << 32), y=base + (4 << 32),
+             B=2, C=8, H=16, W=16, dirs=15, groups=1, ch_per_weight=1)
+    d.update(kw)
+    return _lib.Problem(**d)
+
+
+@pytest.mark.parametrize("probs,kw,code", [
+    ([], {}, -2),
+    ([prob(i) for i in range(33)], {}, -2),
+    ([prob(0)], dict(dtype=3), -6),
+    ([prob(0), prob(1, H=65)], {}, -10),
+    ([prob(0), prob(1, groups=3)], {}, -4),
+    ([prob(0), prob(1, x=0)], {}, -1),
+    ([prob(0), prob(1, y=FAKE + (1 << 36) + (4 << 32) + 8)], {}, -7),
+    ([prob(0), prob(1, y=FAKE + (2 << 32))], {}, -8),              # y of problem 1 on lam of problem 0
+    ([prob(0), prob(1, y=FAKE + (4 << 32) + 256)], {}, -8),        # the two outputs overlap
+])
+def test_batched_invalid_arguments_rejected_on_host(lib, probs, kw, code):
+    assert _lib.scan_fwd_batched_ptr(probs, **kw) == code
