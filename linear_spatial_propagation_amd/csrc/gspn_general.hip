@@ -85,9 +85,15 @@ __global__ __launch_bounds__(kThreads) void direction_kernel(GeneralParams prm) 
                 const float a1 = to_f32(ws[HW + e]);
                 const float a2 = has2 ? to_f32(ws[2 * HW + e]) : 0.0f;
                 const Taps tp = normalise_taps(a0, a1, a2, has0, has2);
-                v = fmaf(tp.w1, hp[p], xl);
-                if (has0) v = fmaf(tp.w0, hp[p - 1], v);
-                if (has2) v = fmaf(tp.w2, hp[p + 1], v);
+                // difference form: the weights sum to exactly 1 (w1 = 1 - w0 -
+                // w2 implicitly), so rounding in the normalisation cannot add a
+                // drift that compounds over thousands of lines
+                const float hc = hp[p];
+                const float hl = has0 ? hp[p - 1] : hc;
+                const float hr = has2 ? hp[p + 1] : hc;
+                v = hc + xl;
+                v = fmaf(tp.w0, hl - hc, v);
+                v = fmaf(tp.w2, hr - hc, v);
             }
             hn[p] = v;
             plane[e] = v;

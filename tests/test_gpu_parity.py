@@ -123,7 +123,15 @@ EDGE_GENERAL = EDGE[:8] + [
     (1, 2, 257, 65, 15, 1, 2),
     (1, 1, 600, 33, 9, 3, 1),
     (2, 4, 96, 80, 15, 16, 2),
+    # the largest accepted side (GSPN_MAX_SIDE = 4096)
+    (1, 1, 4096, 8, 15, 1, 1),
+    (1, 1, 8, 4096, 12, 64, 1),
 ]
+
+
+def test_maximum_grid():
+    """4096 x 4096, the largest grid the ABI accepts, on the per-line fallback."""
+    check(make_workload(1, 1, 4096, 4096, dtype="f32", seed=77), path="general")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
