@@ -292,8 +292,8 @@ def main():
         summarize_stats(args.summarize_stats, args.profile_command, args.config, args.pass_)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this operator has no cross-GPU step, and runs "
-              f"with --gpus {args.gpus} are not part of this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the operator has no cross-GPU step, so "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
