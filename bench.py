@@ -38,6 +38,9 @@ With --variant dirs a step is one call of gspn_scan_fwd_ex with lambda and
 u per direction (y = sum_d u_d * h_d); the algorithmic bytes count the four
 lambda and four u slabs once:
     s * (|x| + ndir |lam| + ndir |u| + |y|) + (taps as for the forward).
+With --pass bwd --variant dirs a step is one call of gspn_scan_bwd_ex (the
+backward of that variant); lambda, u and their gradients count ndir slabs:
+    (the backward's bytes) + s * 4 * (ndir - 1) * |x|.
 
 Prints ONE JSON line.
 """
@@ -56,6 +59,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GSPN scan GB/s and % of HBM peak (4-dir fwd), 1K C-GSPN config"
 METRIC_BWD = "GSPN scan backward GB/s and % of HBM peak (4-dir bwd)"
 METRIC_DIRS = "GSPN scan GB/s and % of HBM peak (4-dir fwd, per-direction lambda and u)"
+METRIC_BWD_DIRS = "GSPN scan backward GB/s and % of HBM peak (4-dir bwd, per-direction lambda and u)"
 HBM_PEAK_GBPS = 8000.0
 COPY_CALIBRATION_BYTES = 256 * 1024 * 1024
 # The dominant kernel of each pass on the default workload (C-GSPN 1K, 64 x 64
@@ -273,7 +277,7 @@ def main():
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the backward")
     ap.add_argument("--variant", choices=("none", "dirs"), default="none",
-                    help="dirs: the forward with per-direction lambda and u (gspn_scan_fwd_ex)")
+                    help="dirs: per-direction lambda and u (gspn_scan_fwd_ex; with --pass bwd, gspn_scan_bwd_ex)")
     ap.add_argument("--batched", type=int, default=1,
                     help="K > 1: K copies of the workload in one batched launch (gspn_scan_fwd_batched)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
@@ -315,6 +319,7 @@ def main():
 
     bwd = args.pass_ == "bwd"
     dirs_variant = args.variant == "dirs" and not bwd
+    bwd_variant = args.variant == "dirs" and bwd
     batched = args.batched if not bwd and not dirs_variant else 1
     base = [up(a) for a in (wl.x_store, wl.w_store, wl.lam_store, wl.u_store)]
     if dirs_variant:
@@ -330,7 +335,13 @@ def main():
         from linear_spatial_propagation_amd.inputs import make_gy
         base.append(up(make_gy(wl, 1000 + cfgd["seed"])))
         nbytes = algorithmic_bytes_bwd(B, C, H, W, 15, wl.groups, wl.cpw, wl.dtype)
-        outs_like = [base[0], base[1], base[0], base[0]]
+        if bwd_variant:
+            from linear_spatial_propagation_amd.inputs import _store
+            rng = np.random.default_rng([cfgd["seed"], 5])
+            for i in (2, 3):
+                base[i] = up(_store(rng.random((4, B, C, H, W), dtype=np.float32), wl.dtype))
+            nbytes += 4 * 3 * B * C * H * W * (2 if wl.dtype == "bf16" else 4)
+        outs_like = [base[0], base[1], base[2], base[3]]
     else:
         nbytes = algorithmic_bytes(B, C, H, W, 15, wl.groups, wl.cpw, wl.dtype)
         outs_like = [base[0]]
@@ -374,6 +385,8 @@ def main():
         ins, outs = sets[i % R]
         if batched > 1:
             _lib.check(batched_fn(barrays[i % R], batched, dtc, stream_handle))
+        elif bwd_variant:
+            gspn.scan_bwd_dirs(*ins, dirs=15, groups=wl.groups, ch_per_weight=wl.cpw, out=outs)
         elif bwd:
             gspn.scan_bwd(*ins, dirs=15, groups=wl.groups, ch_per_weight=wl.cpw, out=outs)
         elif dirs_variant:
@@ -434,10 +447,10 @@ def main():
     value = nbytes * args.steps / elapsed / 1e9
     avg_launch = float(per.mean())
     achieved = nbytes / avg_launch / 1e9
-    traffic = load_traffic(args.pass_) if args.config == "cgspn1k" and not dirs_variant else None
+    traffic = load_traffic(args.pass_) if args.config == "cgspn1k" and args.variant == "none" else None
     E = B * C * H * W
     out = {
-        "metric": METRIC_BWD if bwd else (METRIC_DIRS if dirs_variant else METRIC),
+        "metric": (METRIC_BWD_DIRS if bwd_variant else METRIC_BWD) if bwd else (METRIC_DIRS if dirs_variant else METRIC),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -453,7 +466,8 @@ def main():
             "workload": f"{args.config}: B={B} C={C} H={H} W={W} groups={wl.groups} "
                         f"ch_per_weight={wl.cpw} dirs=TB|BT|LR|RL, {wl.dtype} I/O, fp32 arithmetic",
             "io_dtype": wl.dtype,
-            "path": ("fused backward" if max(H, W) <= 64 else "backward line kernels") if bwd else
+            "path": ("backward line kernels, per-direction lambda and u" if bwd_variant else
+                     "fused backward" if max(H, W) <= 64 else "backward line kernels") if bwd else
                     "line kernels, per-direction lambda and u" if dirs_variant else
                     {1: "fused", 2: "general"}[gspn.select_path(B, C, H, W, groups=wl.groups,
                                                                 ch_per_weight=wl.cpw)],
@@ -482,9 +496,10 @@ def main():
         out["separate_launches_us"] = round(separate_us, 3)
     if bwd:
         # 64 x 64 grids and smaller: one fused kernel per call
-        out["roofline"]["kernel"] = ("fused_bwd_kernel" if max(H, W) <= 64
+        out["roofline"]["kernel"] = ("gspn_scan_bwd_ex, all launches of one call" if bwd_variant else
+                                     "fused_bwd_kernel" if max(H, W) <= 64
                                      else "gspn_scan_bwd, all launches of one call")
-    if not args.no_cpu and not dirs_variant and batched == 1:
+    if not args.no_cpu and args.variant == "none" and batched == 1:
         out["cpu_baseline"] = cpu_baseline(args.config, backward=bwd)
     print(json.dumps(out), flush=True)
 

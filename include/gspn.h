@@ -110,7 +110,7 @@ enum {
     GSPN_ERR_ALIAS = -8,  /* an output overlaps an input or another output */
     GSPN_ERR_HIP = -9,    /* a HIP call failed; see gspn_last_error() */
     GSPN_ERR_PATH = -10,  /* unknown path, or the path (or the backward) cannot take this shape */
-    GSPN_ERR_FLAGS = -11  /* unknown bit in flags (gspn_scan_fwd_ex) */
+    GSPN_ERR_FLAGS = -11  /* unknown bit in flags (gspn_scan_fwd_ex, gspn_scan_bwd_ex) */
 };
 
 /* Flags of gspn_scan_fwd_ex. */
@@ -168,7 +168,7 @@ int gspn_scan_fwd_path(const void *x, const void *w_raw, const void *lam, const 
  * give GSPN_ERR_FLAGS.  With a flag set the call runs the line kernels
  * (H, W <= 512 and multiples of K, else GSPN_ERR_PATH) and, with
  * GSPN_LAM_PER_DIR and LR or RL enabled, its workspace holds one transposed
- * lam per column direction.  No backward is provided for the variants.
+ * lam per column direction.  gspn_scan_bwd_ex is its backward.
  */
 int gspn_scan_fwd_ex(const void *x, const void *w_raw, const void *lam, const void *u, void *y,
                      int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
@@ -255,6 +255,30 @@ int gspn_scan_bwd_path(const void *x, const void *w_raw, const void *lam, const 
                        void *gx, void *gw_raw, void *glam, void *gu, int64_t B, int64_t C, int64_t H,
                        int64_t W, uint32_t dirs, int32_t groups, int32_t ch_per_weight, int32_t dtype,
                        int32_t path, hipStream_t stream);
+
+/*
+ * Backward of gspn_scan_fwd_ex (per-direction lam and/or u): the exact
+ * vector-Jacobian product of y = sum over enabled d of u_d * h_d, h_d the scan
+ * of direction d driven by lam_d * x.  With g_d the adjoint of direction d
+ * (as in gspn_scan_bwd, with u_d in its source term gy * u_d):
+ *   gu_d   = gy * h_d             (GSPN_U_PER_DIR; else gu = gy * sum_d h_d)
+ *   glam_d = x * g_d              (GSPN_LAM_PER_DIR; else glam = x * sum_d g_d)
+ *   gx     = sum_d lam_d * g_d
+ *   gw_raw as in gspn_scan_bwd, from each direction's own g_d and h_d.
+ *   flags : as in gspn_scan_fwd_ex; a flagged input (lam, u) and its
+ *           gradient (glam, gu) are [popcount(dirs)][B][C][H][W], slabs in
+ *           ascending bit order.  flags = 0 is gspn_scan_bwd.
+ * With a flag set the call runs the line kernels (H, W <= 512 and multiples
+ * of K, else GSPN_ERR_PATH); the workspace is that of gspn_scan_bwd, with one
+ * transposed lam (GSPN_LAM_PER_DIR) and one transposed u (GSPN_U_PER_DIR)
+ * per enabled column direction instead of one.  Unknown flag bits give
+ * GSPN_ERR_FLAGS; other errors, aliasing rules and tolerances as
+ * gspn_scan_bwd.
+ */
+int gspn_scan_bwd_ex(const void *x, const void *w_raw, const void *lam, const void *u, const void *gy,
+                     void *gx, void *gw_raw, void *glam, void *gu, int64_t B, int64_t C, int64_t H, int64_t W,
+                     uint32_t dirs, int32_t groups, int32_t ch_per_weight, uint32_t flags, int32_t dtype,
+                     hipStream_t stream);
 
 /* GSPN_OK if gspn_scan_bwd can run these sizes, GSPN_ERR_PATH if the shape is
  * outside its kernels, or another negative code for invalid sizes. */

@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import (DIR_ALL, DIR_BT, DIR_LR, DIR_RL, DIR_TB, PATH_AUTO, PATH_FUSED, PATH_GENERAL,
                    GspnError, load, select_path)
 
-__all__ = ["scan_fwd", "scan_bwd", "scan_fwd_dirs", "scan_fwd_batched", "select_path", "load", "GspnError", "DIR_TB", "DIR_BT", "DIR_LR", "DIR_RL",
+__all__ = ["scan_fwd", "scan_bwd", "scan_fwd_dirs", "scan_bwd_dirs", "scan_fwd_batched", "select_path", "load", "GspnError", "DIR_TB", "DIR_BT", "DIR_LR", "DIR_RL",
            "DIR_ALL", "PATH_AUTO", "PATH_FUSED", "PATH_GENERAL"]
 
 
@@ -130,6 +130,51 @@ def scan_fwd_dirs(x, w_raw, lam, u, *, dirs: int = DIR_ALL, groups: int = 1, ch_
                                   stream=stream)
     _lib.check(rc)
     return out
+
+
+def scan_bwd_dirs(x, w_raw, lam, u, gy, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1,
+                  out=None):
+    """Backward of scan_fwd_dirs (gspn_scan_bwd_ex).
+
+    lam and u as in scan_fwd_dirs; returns (gx, gw_raw, glam, gu) with glam
+    and gu shaped like lam and u (one slab per enabled direction when that
+    input has one).  ``out`` may give the four output tensors.
+    """
+    import torch
+    if x.dim() != 4:
+        raise ValueError("x must be [B, C, H, W]")
+    nd = bin(dirs & 15).count("1")
+    flags = 0
+    shared = {"x": x, "w_raw": w_raw, "gy": gy}
+    for name, t, bit in (("lam", lam, _lib.LAM_PER_DIR), ("u", u, _lib.U_PER_DIR)):
+        if t.dim() == 5:
+            if tuple(t.shape) != (nd,) + tuple(x.shape):
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(nd,) + tuple(x.shape)}")
+            flags |= bit
+            shared[name] = t[0]       # shape and dtype checks on one slab
+        else:
+            shared[name] = t
+    dev, (B, C, H, W) = _check_inputs(shared, dirs, ch_per_weight)
+    for name, t in (("lam", lam), ("u", u)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if out is None:
+        gx, gw, glam, gu = torch.empty_like(x), torch.empty_like(w_raw), torch.empty_like(lam), torch.empty_like(u)
+    else:
+        gx, gw, glam, gu = out
+        for t, like in ((gx, x), (gw, w_raw), (glam, lam), (gu, u)):
+            if (t.shape != like.shape or t.dtype != like.dtype or t.device != dev
+                    or not t.is_contiguous()):
+                raise ValueError("out tensors must be contiguous and shaped like x, w_raw, lam, u")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = _lib.scan_bwd_ex_ptr(x.data_ptr(), w_raw.data_ptr(), lam.data_ptr(), u.data_ptr(),
+                                  gy.data_ptr(), gx.data_ptr(), gw.data_ptr(), glam.data_ptr(),
+                                  gu.data_ptr(), B, C, H, W, dirs=dirs, groups=groups,
+                                  ch_per_weight=ch_per_weight, flags=flags, dtype=_dtype_code(x),
+                                  stream=stream)
+    _lib.check(rc)
+    return gx, gw, glam, gu
 
 
 def scan_fwd_batched(problems):

@@ -33,7 +33,7 @@ class Problem(ctypes.Structure):
 
 EXPORTED = ("gspn_scan_fwd", "gspn_scan_fwd_path", "gspn_scan_fwd_ex", "gspn_scan_fwd_batched",
             "gspn_select_path", "gspn_scan_bwd",
-            "gspn_scan_bwd_path", "gspn_bwd_supported", "gspn_status_string", "gspn_last_error", "gspn_version")
+            "gspn_scan_bwd_path", "gspn_scan_bwd_ex", "gspn_bwd_supported", "gspn_status_string", "gspn_last_error", "gspn_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -71,6 +71,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.gspn_scan_bwd.restype = ctypes.c_int
         lib.gspn_scan_bwd_path.argtypes = [vp] * 9 + [i64, i64, i64, i64, u32, i32, i32, i32, i32, vp]
         lib.gspn_scan_bwd_path.restype = ctypes.c_int
+        lib.gspn_scan_bwd_ex.argtypes = [vp] * 9 + [i64, i64, i64, i64, u32, i32, i32, u32, i32, vp]
+        lib.gspn_scan_bwd_ex.restype = ctypes.c_int
         lib.gspn_bwd_supported.argtypes = [i64, i64, i64, i64, u32, i32, i32, i32]
         lib.gspn_bwd_supported.restype = ctypes.c_int
         lib.gspn_status_string.argtypes = [ctypes.c_int]
@@ -124,6 +126,14 @@ def scan_bwd_ptr(x: int, w: int, lam: int, u: int, gy: int, gx: int, gw: int, gl
     """Raw backward call on device pointers; returns the status code."""
     return load().gspn_scan_bwd_path(x, w, lam, u, gy, gx, gw, glam, gu, B, C, H, W, dirs, groups,
                                      ch_per_weight, dtype, path, stream)
+
+
+def scan_bwd_ex_ptr(x: int, w: int, lam: int, u: int, gy: int, gx: int, gw: int, glam: int, gu: int,
+                    B: int, C: int, H: int, W: int, *, dirs: int = DIR_ALL, groups: int = 1,
+                    ch_per_weight: int = 1, flags: int = 0, dtype: int = GSPN_BF16, stream: int = 0) -> int:
+    """Raw backward of the per-direction variant on device pointers; returns the status code."""
+    return load().gspn_scan_bwd_ex(x, w, lam, u, gy, gx, gw, glam, gu, B, C, H, W, dirs, groups,
+                                   ch_per_weight, flags, dtype, stream)
 
 
 def bwd_supported(B, C, H, W, *, dirs=DIR_ALL, groups=1, ch_per_weight=1, dtype=GSPN_BF16) -> int:

@@ -84,6 +84,68 @@ int gspn_select_path(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, 
 
 namespace {
 
+// The backward of gspn_scan_fwd (flags = 0) and of its per-direction
+// variants (gspn_scan_fwd_ex's flags; line kernels only).
+int scan_bwd_impl(const void* x, const void* w_raw, const void* lam, const void* u, const void* gy, void* gx,
+                  void* gw_raw, void* glam, void* gu, int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs,
+                  int32_t groups, int32_t ch_per_weight, uint32_t flags, int32_t dtype, int32_t path,
+                  hipStream_t stream) {
+    g_last_error[0] = '\0';
+    int rc = check_sizes(B, C, H, W, dirs, groups, ch_per_weight, dtype);
+    if (rc) return rc;
+    if (flags & ~(uint32_t)(GSPN_LAM_PER_DIR | GSPN_U_PER_DIR)) return GSPN_ERR_FLAGS;
+    if (!x || !w_raw || !lam || !u || !gy || !gx || !gw_raw || !glam || !gu) return GSPN_ERR_NULL;
+    const void* ptrs[9] = {x, w_raw, lam, u, gy, gx, gw_raw, glam, gu};
+    for (const void* q : ptrs)
+        if ((uintptr_t)q & 15u) return GSPN_ERR_ALIGN;
+    const size_t es = dtype == GSPN_BF16 ? 2 : 4;
+    const size_t nbytes = (size_t)B * C * H * W * es;
+    const size_t wbytes = (size_t)popcount4(dirs) * B * (C / ch_per_weight) * 3 * H * W * es;
+    const size_t lbytes = (flags & GSPN_LAM_PER_DIR) ? popcount4(dirs) * nbytes : nbytes;
+    const size_t ubytes = (flags & GSPN_U_PER_DIR) ? popcount4(dirs) * nbytes : nbytes;
+    // every output is disjoint from every input and from the other outputs
+    const void* outs[4] = {gx, gw_raw, glam, gu};
+    const size_t out_bytes[4] = {nbytes, wbytes, lbytes, ubytes};
+    const void* ins[5] = {x, w_raw, lam, u, gy};
+    const size_t in_bytes[5] = {nbytes, wbytes, lbytes, ubytes, nbytes};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return GSPN_ERR_ALIAS;
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return GSPN_ERR_ALIAS;
+    }
+    // per-direction lambda / u run on the line kernels only
+    if (path == GSPN_PATH_AUTO) path = flags ? GSPN_PATH_GENERAL : auto_path(H, W);
+    if (path != GSPN_PATH_FUSED && path != GSPN_PATH_GENERAL) return GSPN_ERR_PATH;
+    if (path == GSPN_PATH_FUSED && (auto_path(H, W) != GSPN_PATH_FUSED || flags)) return GSPN_ERR_PATH;
+    if (path == GSPN_PATH_GENERAL && !gspn::lines_supported((int)H, (int)W)) {
+        set_error_text("the backward runs on the line kernels: H, W <= 512 and multiples of K");
+        return GSPN_ERR_PATH;
+    }
+
+    gspn::GradArgs g;
+    g.fwd.x = x; g.fwd.w = w_raw; g.fwd.lam = lam; g.fwd.u = u; g.fwd.y = nullptr;
+    g.fwd.B = (int)B; g.fwd.C = (int)C; g.fwd.H = (int)H; g.fwd.W = (int)W;
+    g.fwd.dirs = dirs; g.fwd.groups = groups; g.fwd.cpw = ch_per_weight; g.fwd.bf16 = dtype == GSPN_BF16;
+    g.fwd.lam_dir = (flags & GSPN_LAM_PER_DIR) != 0;
+    g.fwd.u_dir = (flags & GSPN_U_PER_DIR) != 0;
+    g.gy = gy; g.gx = gx; g.gw = gw_raw; g.glam = glam; g.gu = gu;
+    if (path == GSPN_PATH_FUSED) {
+        const hipError_t e = gspn::launch_fused_bwd(g, stream);
+        if (e != hipSuccess) { set_error("fused backward launch", e); return GSPN_ERR_HIP; }
+        return GSPN_OK;
+    }
+    void* work = nullptr;
+    hipError_t e = hipMallocAsync(&work, gspn::lines_bwd_workspace_bytes(g), stream);
+    if (e != hipSuccess) { set_error("hipMallocAsync(workspace)", e); return GSPN_ERR_HIP; }
+    e = gspn::launch_lines_bwd(g, work, stream);
+    const hipError_t ef = hipFreeAsync(work, stream);
+    if (e != hipSuccess) { set_error("backward kernel launch", e); return GSPN_ERR_HIP; }
+    if (ef != hipSuccess) { set_error("hipFreeAsync(workspace)", ef); return GSPN_ERR_HIP; }
+    return GSPN_OK;
+}
+
+
 int scan_fwd_impl(const void* x, const void* w_raw, const void* lam, const void* u, void* y, int64_t B,
                   int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups, int32_t ch_per_weight,
                   uint32_t flags, int32_t dtype, int32_t path, hipStream_t stream) {
@@ -227,54 +289,16 @@ int gspn_scan_bwd_path(const void* x, const void* w_raw, const void* lam, const 
                        void* gx, void* gw_raw, void* glam, void* gu, int64_t B, int64_t C, int64_t H,
                        int64_t W, uint32_t dirs, int32_t groups, int32_t ch_per_weight, int32_t dtype,
                        int32_t path, hipStream_t stream) {
-    g_last_error[0] = '\0';
-    int rc = check_sizes(B, C, H, W, dirs, groups, ch_per_weight, dtype);
-    if (rc) return rc;
-    if (!x || !w_raw || !lam || !u || !gy || !gx || !gw_raw || !glam || !gu) return GSPN_ERR_NULL;
-    const void* ptrs[9] = {x, w_raw, lam, u, gy, gx, gw_raw, glam, gu};
-    for (const void* q : ptrs)
-        if ((uintptr_t)q & 15u) return GSPN_ERR_ALIGN;
-    const size_t es = dtype == GSPN_BF16 ? 2 : 4;
-    const size_t nbytes = (size_t)B * C * H * W * es;
-    const size_t wbytes = (size_t)popcount4(dirs) * B * (C / ch_per_weight) * 3 * H * W * es;
-    // every output is disjoint from every input and from the other outputs
-    const void* outs[4] = {gx, gw_raw, glam, gu};
-    const size_t out_bytes[4] = {nbytes, wbytes, nbytes, nbytes};
-    const void* ins[5] = {x, w_raw, lam, u, gy};
-    const size_t in_bytes[5] = {nbytes, wbytes, nbytes, nbytes, nbytes};
-    for (int i = 0; i < 4; ++i) {
-        for (int j = 0; j < 5; ++j)
-            if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return GSPN_ERR_ALIAS;
-        for (int j = 0; j < i; ++j)
-            if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return GSPN_ERR_ALIAS;
-    }
-    if (path == GSPN_PATH_AUTO) path = auto_path(H, W);
-    if (path != GSPN_PATH_FUSED && path != GSPN_PATH_GENERAL) return GSPN_ERR_PATH;
-    if (path == GSPN_PATH_FUSED && auto_path(H, W) != GSPN_PATH_FUSED) return GSPN_ERR_PATH;
-    if (path == GSPN_PATH_GENERAL && !gspn::lines_supported((int)H, (int)W)) {
-        set_error_text("the backward runs on the line kernels: H, W <= 512 and multiples of K");
-        return GSPN_ERR_PATH;
-    }
+    return scan_bwd_impl(x, w_raw, lam, u, gy, gx, gw_raw, glam, gu, B, C, H, W, dirs, groups, ch_per_weight, 0u,
+                         dtype, path, stream);
+}
 
-    gspn::GradArgs g;
-    g.fwd.x = x; g.fwd.w = w_raw; g.fwd.lam = lam; g.fwd.u = u; g.fwd.y = nullptr;
-    g.fwd.B = (int)B; g.fwd.C = (int)C; g.fwd.H = (int)H; g.fwd.W = (int)W;
-    g.fwd.dirs = dirs; g.fwd.groups = groups; g.fwd.cpw = ch_per_weight; g.fwd.bf16 = dtype == GSPN_BF16;
-    g.fwd.lam_dir = 0; g.fwd.u_dir = 0;
-    g.gy = gy; g.gx = gx; g.gw = gw_raw; g.glam = glam; g.gu = gu;
-    if (path == GSPN_PATH_FUSED) {
-        const hipError_t e = gspn::launch_fused_bwd(g, stream);
-        if (e != hipSuccess) { set_error("fused backward launch", e); return GSPN_ERR_HIP; }
-        return GSPN_OK;
-    }
-    void* work = nullptr;
-    hipError_t e = hipMallocAsync(&work, gspn::lines_bwd_workspace_bytes(g), stream);
-    if (e != hipSuccess) { set_error("hipMallocAsync(workspace)", e); return GSPN_ERR_HIP; }
-    e = gspn::launch_lines_bwd(g, work, stream);
-    const hipError_t ef = hipFreeAsync(work, stream);
-    if (e != hipSuccess) { set_error("backward kernel launch", e); return GSPN_ERR_HIP; }
-    if (ef != hipSuccess) { set_error("hipFreeAsync(workspace)", ef); return GSPN_ERR_HIP; }
-    return GSPN_OK;
+int gspn_scan_bwd_ex(const void* x, const void* w_raw, const void* lam, const void* u, const void* gy,
+                     void* gx, void* gw_raw, void* glam, void* gu, int64_t B, int64_t C, int64_t H, int64_t W,
+                     uint32_t dirs, int32_t groups, int32_t ch_per_weight, uint32_t flags, int32_t dtype,
+                     hipStream_t stream) {
+    return scan_bwd_impl(x, w_raw, lam, u, gy, gx, gw_raw, glam, gu, B, C, H, W, dirs, groups, ch_per_weight,
+                         flags, dtype, GSPN_PATH_AUTO, stream);
 }
 
 }  // extern "C"

@@ -14,6 +14,9 @@
 //   dL/da_t = w_t (1 - sigmoid(a_t)) (dL/dw_t - sum_v dL/dw_v w_v)
 //         (sigmoid-then-normalise; 0 on the taps the forward never reads),
 //         evaluated from E0 = D0 - D1, E2 = D2 - D1 without cancellation.
+// With per-direction lambda_d / u_d (the variants y = sum_d u_d h_d, h_d
+// driven by lambda_d x) the adjoint of direction d takes gy * u_d as its
+// source, gu_d = gy * h_d, glam_d = x * g_d and gx = sum_d lambda_d g_d.
 //
 // Launches, in order, on the caller's stream:
 //  1. transpose_kernel: x, lambda, gy, u and the LR/RL raw taps to [W][H];
@@ -37,9 +40,10 @@ namespace {
 
 struct AdjointParams {
     const void* gy;     // [B][C][H][W]
-    const void* u;
+    const void* u;      // [B][C][H][W], or one slab per enabled direction (u_ds apart)
     const void* gyT;    // [B][C][W][H] (when LR or RL is enabled)
-    const void* uT;
+    const void* uT;     // transposed u, one slab per column direction when per direction
+    size_t u_ds, uT_ds; // elements between u slabs (0: shared)
     const void* w;      // raw taps [nd][B][Cw][3][H][W]
     const void* wT;     // [ncol][B][Cw][3][W][H]
     float* planes;      // [nd][B][C][n][m]: h on entry, the adjoint g on exit
@@ -109,7 +113,9 @@ __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
 
     // every tensor is read as [n][m], line-major; channel ch at + ch * HW
     const T* gys = static_cast<const T*>(is_row ? prm.gy : prm.gyT) + ((size_t)b * C + cbase) * HW;
-    const T* us = static_cast<const T*>(is_row ? prm.u : prm.uT) + ((size_t)b * C + cbase) * HW;
+    const T* us = (is_row ? static_cast<const T*>(prm.u) + slot * prm.u_ds
+                          : static_cast<const T*>(prm.uT) + prm.col_index[slot] * prm.uT_ds) +
+                  ((size_t)b * C + cbase) * HW;
     const T* ws = is_row
         ? static_cast<const T*>(prm.w) + ((size_t)(slot * B + b) * Cw + k) * 3 * HW
         : static_cast<const T*>(prm.wT) + ((size_t)(prm.col_index[slot] * B + b) * Cw + k) * 3 * HW;
@@ -362,9 +368,9 @@ BwdLayout bwd_layout(const GradArgs& g) {
     l.xT = l.lamT = l.gyT = l.uT = l.wT = 0;
     if (ncol) {
         l.xT = o;   o += align256(E * es);
-        l.lamT = o; o += align256(E * es);
+        l.lamT = o; o += align256((a.lam_dir ? ncol : 1) * E * es);
         l.gyT = o;  o += align256(E * es);
-        l.uT = o;   o += align256(E * es);
+        l.uT = o;   o += align256((a.u_dir ? ncol : 1) * E * es);
         l.wT = o;   o += align256((size_t)ncol * Ew * es);
     }
     l.ga = o; o += align256((size_t)nd * Ew * sizeof(float));
@@ -393,8 +399,9 @@ hipError_t launch_lines_bwd_t(const GradArgs& g, void* workspace, hipStream_t st
     p.xT = xT; p.lamT = lamT; p.wT = wT;
     p.planes = planes;
     p.sink = sink;
-    p.lam_ds = 0;   // the backward takes lambda and u shared by all directions
-    p.lamT_ds = 0;
+    const size_t E = (size_t)a.B * a.C * H * W;
+    p.lam_ds = a.lam_dir ? E : 0;    // per-direction lambda: one slab per slot
+    p.lamT_ds = a.lam_dir ? E : 0;   // and one transposed slab per column direction
     p.B = a.B; p.C = a.C; p.H = H; p.W = W; p.Cw = Cw; p.cpw = a.cpw; p.groups = a.groups;
     int ncol = 0;
     p.nd = enabled_slots(a.dirs, p.dir_of_slot, p.col_index, &ncol);
@@ -405,27 +412,50 @@ hipError_t launch_lines_bwd_t(const GradArgs& g, void* workspace, hipStream_t st
     // 1. column-major copies for LR / RL
     if (ncol > 0) {
         launch_transpose(static_cast<const T*>(a.x), xT, slices, H, W, stream);
-        launch_transpose(static_cast<const T*>(a.lam), lamT, slices, H, W, stream);
         launch_transpose(static_cast<const T*>(g.gy), gyT, slices, H, W, stream);
-        launch_transpose(static_cast<const T*>(a.u), uT, slices, H, W, stream);
+        if (!a.lam_dir) launch_transpose(static_cast<const T*>(a.lam), lamT, slices, H, W, stream);
+        if (!a.u_dir) launch_transpose(static_cast<const T*>(a.u), uT, slices, H, W, stream);
         for (int s = 0; s < p.nd; ++s) {
             if (p.dir_of_slot[s] < 2) continue;
+            if (a.lam_dir)
+                launch_transpose(static_cast<const T*>(a.lam) + (size_t)s * E, lamT + (size_t)p.col_index[s] * E,
+                                 slices, H, W, stream);
+            if (a.u_dir)
+                launch_transpose(static_cast<const T*>(a.u) + (size_t)s * E, uT + (size_t)p.col_index[s] * E,
+                                 slices, H, W, stream);
             launch_transpose(static_cast<const T*>(a.w) + (size_t)s * wslab * HW,
                              wT + (size_t)p.col_index[s] * wslab * HW, wslab, H, W, stream);
         }
     }
     // 2. forward states
     launch_line_scan<T>(p, stream);
-    // 3. gu = gy * sum_dir h_dir
+    // 3. gu = gy * sum_dir h_dir, or gu_d = gy * h_d per direction
     MergeParams q;
     q.planes = planes;
     q.B = a.B; q.C = a.C; q.H = H; q.W = W; q.nd = p.nd;
     for (int s = 0; s < 4; ++s) q.dir_of_slot[s] = p.dir_of_slot[s];
     q.in[0] = g.gy; q.out[0] = g.gu; q.in[1] = nullptr; q.out[1] = nullptr;
-    launch_merge<T, 1>(q, stream);
+    // one direction's plane: the merge of a single slot
+    auto one_slot = [&](MergeParams m, int s) {
+        m.planes = planes + (size_t)s * E;
+        m.nd = 1;
+        m.dir_of_slot[0] = p.dir_of_slot[s];
+        return m;
+    };
+    if (a.u_dir) {
+        for (int s = 0; s < p.nd; ++s) {
+            MergeParams m = one_slot(q, s);
+            m.out[0] = static_cast<T*>(g.gu) + (size_t)s * E;
+            launch_merge<T, 1>(m, stream);
+        }
+    } else {
+        launch_merge<T, 1>(q, stream);
+    }
     // 4. adjoint scans, one launch per chunk of channels
     AdjointParams r;
     r.gy = g.gy; r.u = a.u; r.gyT = gyT; r.uT = uT; r.w = a.w; r.wT = wT;
+    r.u_ds = a.u_dir ? E : 0;
+    r.uT_ds = a.u_dir ? E : 0;
     r.planes = planes; r.ga = ga; r.sink = sink;
     r.B = a.B; r.C = a.C; r.H = H; r.W = W; r.Cw = Cw; r.cpw = a.cpw; r.groups = a.groups; r.nd = p.nd;
     for (int s = 0; s < 4; ++s) { r.dir_of_slot[s] = p.dir_of_slot[s]; r.col_index[s] = p.col_index[s]; }
@@ -436,9 +466,21 @@ hipError_t launch_lines_bwd_t(const GradArgs& g, void* workspace, hipStream_t st
         r.chunk = c;
         launch_adjoint<T>(r, K, CH, c > 0, stream);
     }
-    // 5. gx = lam * G, glam = x * G
-    q.in[0] = a.lam; q.out[0] = g.gx; q.in[1] = a.x; q.out[1] = g.glam;
-    launch_merge<T, 2>(q, stream);
+    // 5. gx = lam * G, glam = x * G; per-direction lambda:
+    //    gx = sum_d lam_d * g_d, glam_d = x * g_d
+    if (a.lam_dir) {
+        q.in[0] = a.lam; q.out[0] = g.gx; q.in[1] = nullptr; q.out[1] = nullptr;
+        launch_merge_dirs<T>(q, stream);
+        for (int s = 0; s < p.nd; ++s) {
+            MergeParams m = one_slot(q, s);
+            m.in[0] = a.x;
+            m.out[0] = static_cast<T*>(g.glam) + (size_t)s * E;
+            launch_merge<T, 1>(m, stream);
+        }
+    } else {
+        q.in[0] = a.lam; q.out[0] = g.gx; q.in[1] = a.x; q.out[1] = g.glam;
+        launch_merge<T, 2>(q, stream);
+    }
     // 6. tap gradients in the caller's layout and dtype
     const size_t slab = wslab * HW;
     for (int s = 0; s < p.nd; ++s) {

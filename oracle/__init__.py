@@ -142,6 +142,44 @@ def scan_bwd(x, w, lam, u, gy, *, dirs: int = 15, groups: int = 1, cpw: int = 1,
     return gx, gw, glam, gu
 
 
+def scan_bwd_dirs(x, w, lam, u, gy, *, dirs: int = 15, groups: int = 1, cpw: int = 1,
+                  nthreads: int = 0, lib=None):
+    """Gradients (gx, gw, glam, gu) in fp64 of the per-direction variant
+    y = sum_d u_d * h_d, h_d driven by lam_d * x, for dL/dy = gy.
+
+    lam and u are [B][C][H][W] (shared) or [popcount(dirs)][B][C][H][W];
+    glam and gu have the shapes of lam and u.  y is the sum of
+    single-direction scans, each reading x, its own slab of w, lam_d and u_d,
+    so each gradient is the sum over directions of the single-direction
+    backward above (a shared lam or u collects every direction's term).
+    """
+    x, w, lam, u, gy = (_f64c(a) for a in (x, w, lam, u, gy))
+    gx = np.zeros_like(x)
+    gw = np.empty_like(w)
+    glam = np.zeros_like(lam)
+    gu = np.zeros_like(u)
+    slab = 0
+    for d in range(4):
+        if not (dirs >> d) & 1:
+            continue
+        lam_d = lam[slab] if lam.ndim == 5 else lam
+        u_d = u[slab] if u.ndim == 5 else u
+        gx_d, gw_d, glam_d, gu_d = scan_bwd(x, w[slab:slab + 1], lam_d, u_d, gy, dirs=1 << d, groups=groups,
+                                            cpw=cpw, nthreads=nthreads, lib=lib)
+        gx += gx_d
+        gw[slab] = gw_d[0]
+        if lam.ndim == 5:
+            glam[slab] = glam_d
+        else:
+            glam += glam_d
+        if u.ndim == 5:
+            gu[slab] = gu_d
+        else:
+            gu += gu_d
+        slab += 1
+    return gx, gw, glam, gu
+
+
 def slice_fwd(x, w, lam, u, *, dirs: int = 15, groups: int = 1) -> np.ndarray:
     """One slice: x, lam, u [H][W]; w [popcount(dirs)][3][H][W] -> y [H][W]."""
     x, w, lam, u = (_f64c(a) for a in (x, w, lam, u))

@@ -194,3 +194,30 @@ def prob(i=0, **kw):
 ])
 def test_batched_invalid_arguments_rejected_on_host(lib, probs, kw, code):
     assert _lib.scan_fwd_batched_ptr(probs, **kw) == code
+
+
+def call_bwd_ex(**kw):
+    names = ("x", "w", "lam", "u", "gy", "gx", "gw", "glam", "gu")
+    args = {nm: FAKE + (i << 32) for i, nm in enumerate(names)}
+    args.update(B=2, C=8, H=16, W=16, dirs=15, groups=1, ch_per_weight=1, flags=3, dtype=1)
+    args.update(kw)
+    return _lib.scan_bwd_ex_ptr(*(args[nm] for nm in names), args["B"], args["C"], args["H"], args["W"],
+                                dirs=args["dirs"], groups=args["groups"], ch_per_weight=args["ch_per_weight"],
+                                flags=args["flags"], dtype=args["dtype"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=4), -11), (dict(flags=0x10), -11),
+    (dict(B=0), -2), (dict(dirs=0), -3), (dict(groups=3), -4), (dict(ch_per_weight=3), -5),
+    (dict(dtype=2), -6), (dict(lam=0), -1), (dict(gu=0), -1), (dict(glam=FAKE + (7 << 32) + 4), -7),
+    (dict(gx=FAKE + (2 << 32) + 3 * NBYTES), -8),           # gx inside the last lambda slab
+    (dict(gx=FAKE + (8 << 32) + 2 * NBYTES), -8),           # gx inside the third gu slab
+    (dict(H=130), -10), (dict(flags=3, W=600), -10),
+])
+def test_variant_bwd_invalid_arguments_rejected_on_host(lib, kw, code):
+    assert call_bwd_ex(**kw) == code
+
+
+def test_variant_bwd_flags_zero_is_the_shared_backward(lib):
+    assert call_bwd_ex(flags=0, H=130) == call_bwd(H=130) == -10
+    assert call_bwd_ex(flags=0, gx=FAKE) == -8
