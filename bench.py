@@ -213,9 +213,10 @@ def summarize_pmc(pmc_dir, command, config="cgspn1k", pass_="fwd"):
     print("\n".join(lines))
 
 
-def summarize_stats(stats_csv, command, config="cgspn1k", pass_="fwd"):
+def summarize_stats(stats_csv, command, config="cgspn1k", pass_="fwd", name=None):
     """Copy the kernel rows of a rocprofv3 --kernel-trace --stats CSV into the
-    stats summary under profiles/."""
+    stats summary under profiles/ (named for `name`, default the pass's
+    dominant kernel on the default workload)."""
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [f"# rocprofv3 --kernel-trace --stats summary, workload {config}",
@@ -224,8 +225,12 @@ def summarize_stats(stats_csv, command, config="cgspn1k", pass_="fwd"):
     for r in rows:
         lines.append(f"{_kernel_short(r['Name'])}, {r['Calls']}, {r['TotalDurationNs']}, "
                      f"{float(r['AverageNs']):.1f}, {r['MinNs']}, {r['MaxNs']}, {float(r['Percentage']):.2f}")
-    lines.append(f"kernel_source_hash: {kernel_source_hash(pass_)}")
-    with open(profile_path(pass_, "stats", config), "w") as f:
+    out = profile_path(pass_, "stats", config)
+    if name:
+        out = os.path.join(ROOT, "profiles", f"{name}_{config}_stats.txt")
+    else:
+        lines.append(f"kernel_source_hash: {kernel_source_hash(pass_)}")
+    with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -288,6 +293,8 @@ def main():
                     help="also run one plain 256 MiB device copy (for counter calibration)")
     ap.add_argument("--summarize-pmc", metavar="DIR",
                     help="write the traffic summary from rocprofv3 --pmc output in DIR and exit")
+    ap.add_argument("--profile-name", default=None,
+                    help="file-name stem of the --summarize-stats summary (default: the dominant kernel)")
     ap.add_argument("--summarize-stats", metavar="CSV",
                     help="write the kernel-time summary from a rocprofv3 --stats CSV and exit")
     ap.add_argument("--profile-command", default="", help="command line recorded in the summary")
@@ -296,7 +303,8 @@ def main():
         summarize_pmc(args.summarize_pmc, args.profile_command, args.config, args.pass_)
         return
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats, args.profile_command, args.config, args.pass_)
+        summarize_stats(args.summarize_stats, args.profile_command, args.config, args.pass_,
+                        args.profile_name)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the operator has no cross-GPU step, so "

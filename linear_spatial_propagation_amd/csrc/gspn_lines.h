@@ -18,6 +18,8 @@ namespace gspn {
 namespace {
 
 constexpr int kDepth = 4;   // lines prefetched ahead
+constexpr int kDepthK4 = 8; // the line scan with 4 positions per lane (sides 129..256), whose
+                            // waves are memory-latency bound; with 8 per lane they are not
 constexpr size_t kSinkBytes = 64 * 8 * sizeof(float);
 
 // 16-byte vector <-> floats
@@ -163,7 +165,9 @@ struct LineData {
     LineVec<T, K> a[3], x, l;
 };
 
-template <typename T, int K>
+// D: lines loaded ahead (deeper for long lines: fewer waves share the GPU
+// then, so each must keep more bytes in flight).
+template <typename T, int K, int D>
 __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
     const int lane = threadIdx.x & 63;
     const int unit = blockIdx.x * 4 + uniform(threadIdx.x >> 6);   // (slot, b, c), c fastest
@@ -223,19 +227,19 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
         q.l.load(ls + o);
     };
 
-    LineData<T, K> buf[kDepth];
+    LineData<T, K> buf[D];
 #pragma unroll
-    for (int s = 0; s < kDepth; ++s) load_line(buf[s], min(s, n - 1));
+    for (int s = 0; s < D; ++s) load_line(buf[s], min(s, n - 1));
 
     float h[K];
 #pragma unroll
     for (int e = 0; e < K; ++e) h[e] = 0.0f;
 
-    // kDepth lines per iteration; steps past the last line (when kDepth
-    // does not divide n) compute on clamped data and store nothing
-    for (int i0 = 0; i0 < n; i0 += kDepth) {
+    // D lines per iteration; steps past the last line (when D does not
+    // divide n) compute on clamped data and store nothing
+    for (int i0 = 0; i0 < n; i0 += D) {
 #pragma unroll
-        for (int s = 0; s < kDepth; ++s) {
+        for (int s = 0; s < D; ++s) {
             const int i = i0 + s;
             const LineData<T, K>& q = buf[s];
             float xl[K], a0[K], a1[K], a2[K];
@@ -306,9 +310,9 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
                         *reinterpret_cast<float4*>(dst + e) = make_float4(h[e], h[e + 1], h[e + 2], h[e + 3]);
                 }
             }
-            // refill the slot with the line kDepth ahead (clamped: no
+            // refill the slot with the line D ahead (clamped: no
             // condition), after its data has been used
-            load_line(buf[s], min(i + kDepth, n - 1));
+            load_line(buf[s], min(i + D, n - 1));
         }
     }
 }
@@ -586,10 +590,10 @@ void launch_line_scan(const LineParams& p, hipStream_t stream) {
     const long units = (long)p.nd * p.B * p.C;
     const dim3 grid((unsigned)((units + 3) / 4));
     const int m = p.H > p.W ? p.H : p.W;
-    if (m <= 64) hipLaunchKernelGGL((line_scan_kernel<T, 1>), grid, dim3(256), 0, stream, p);
-    else if (m <= 128) hipLaunchKernelGGL((line_scan_kernel<T, 2>), grid, dim3(256), 0, stream, p);
-    else if (m <= 256) hipLaunchKernelGGL((line_scan_kernel<T, 4>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((line_scan_kernel<T, 8>), grid, dim3(256), 0, stream, p);
+    if (m <= 64) hipLaunchKernelGGL((line_scan_kernel<T, 1, kDepth>), grid, dim3(256), 0, stream, p);
+    else if (m <= 128) hipLaunchKernelGGL((line_scan_kernel<T, 2, kDepth>), grid, dim3(256), 0, stream, p);
+    else if (m <= 256) hipLaunchKernelGGL((line_scan_kernel<T, 4, kDepthK4>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((line_scan_kernel<T, 8, kDepth>), grid, dim3(256), 0, stream, p);
 }
 
 template <typename T>
