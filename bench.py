@@ -20,6 +20,9 @@ events on the stream it runs on (the per-launch durations of the roofline
 figure).  The plain forward and backward steps call the C ABI directly with
 argument tuples built once.
 
+device_copy_gbps: a plain 512 MiB device-to-device copy on the same GPU
+(read + write bytes per second), the practical streaming ceiling, for context.
+
 value = algorithmic bytes x K / elapsed time (GB/s, 1e9 B/s).  Algorithmic
 bytes count each input once, y once, and only the taps the method consumes:
     s * (|x| + |lam| + |u| + |y|) + s * B * Cw * sum_d (n_d - g) * (3 m_d - 2)
@@ -478,6 +481,22 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize(dev)
 
+    # practical ceiling, for context: a plain device-to-device copy of
+    # 2 x 512 MiB buffers (read + write bytes per second), median of 20
+    copy_gbps = None
+    if batched == 1:
+        csrc = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+        cdst = torch.empty_like(csrc)
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        cdst.copy_(csrc)
+        for a, b in cev:
+            a.record(stream)
+            cdst.copy_(csrc)
+            b.record(stream)
+        torch.cuda.synchronize(dev)
+        copy_gbps = round(2 * csrc.numel() / float(np.median([a.elapsed_time(b) for a, b in cev]) * 1e-3) / 1e9, 1)
+        del csrc, cdst
+
     ms_per_step = elapsed / args.steps * 1e3
     value = nbytes * args.steps / elapsed / 1e9
     avg_launch = float(per.mean())
@@ -516,6 +535,7 @@ def main():
                       "median": round(float(np.median(per)) * 1e6, 3),
                       "p90": round(float(np.percentile(per, 90)) * 1e6, 3)},
         "hot_cache_gbps": round(nbytes / float(np.median(hot)) / 1e9, 2),
+        "device_copy_gbps": copy_gbps,
         "wall_s": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},

@@ -50,6 +50,30 @@ def parity_error(y: np.ndarray, yhat: np.ndarray, dtype: str) -> float:
     return float((diff / scale).max()) if y.size else 0.0
 
 
+def rne_bf16(yhat: np.ndarray) -> np.ndarray:
+    """fp64 values rounded once to the nearest bf16 (ties to even), as fp64."""
+    yhat = np.asarray(yhat, dtype=np.float64)
+    ulp = ulp_bf16(yhat)
+    safe = np.where(ulp == 0, 1.0, ulp)
+    return np.where(ulp == 0, 0.0, np.round(yhat / safe) * safe)   # np.round: half to even
+
+
+def diagnostics(y: np.ndarray, yhat: np.ndarray, dtype: str) -> dict:
+    """Side figures of a comparison (reported, not asserted): the unfloored
+    pointwise maximum relative error, the L2-relative error and, for bf16,
+    the fraction of outputs that differ from the correctly rounded exact value."""
+    y = np.asarray(y, dtype=np.float64)
+    yhat = np.asarray(yhat, dtype=np.float64)
+    nz = yhat != 0
+    out = {
+        "pointwise_max": float((np.abs(y - yhat)[nz] / np.abs(yhat[nz])).max()) if nz.any() else 0.0,
+        "l2_rel": float(np.linalg.norm(y - yhat) / max(np.linalg.norm(yhat), 1e-300)),
+    }
+    if dtype == "bf16":
+        out["frac_not_rne"] = float(np.mean(y != rne_bf16(yhat)))
+    return out
+
+
 def to_device(a: np.ndarray, dtype: str):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(a))

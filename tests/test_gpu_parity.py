@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import TOL, from_device, parity_error, run_workload, say, to_device
+from parity import TOL, diagnostics, from_device, parity_error, run_workload, say, to_device
 from linear_spatial_propagation_amd.inputs import (CONFIGS, config_workload, make_workload,
                                                    slice_inputs_f64)
 
@@ -25,7 +25,8 @@ def check(wl, path="auto", tol=None):
     y = run_workload(wl, PATHS[path])
     yhat = oracle.scan_fwd(wl.x, wl.w, wl.lam, wl.u, dirs=wl.dirs, groups=wl.groups, cpw=wl.cpw)
     err = parity_error(y, yhat, wl.dtype)
-    say(f"  err={err:.3e}")
+    diag = diagnostics(y, yhat, wl.dtype)
+    say(f"  err={err:.3e}  " + " ".join(f"{k}={v:.3e}" for k, v in diag.items()))
     assert err <= (tol or TOL[wl.dtype]), err
     return y, yhat
 
