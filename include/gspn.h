@@ -113,7 +113,7 @@ enum {
     GSPN_ERR_FLAGS = -11  /* unknown bit in flags (gspn_scan_fwd_ex, gspn_scan_bwd_ex) */
 };
 
-/* Flags of gspn_scan_fwd_ex. */
+/* Flags of gspn_scan_fwd_ex and gspn_scan_bwd_ex. */
 enum {
     GSPN_LAM_PER_DIR = 1, /* lam holds one [B][C][H][W] slab per enabled direction */
     GSPN_U_PER_DIR = 2    /* u holds one slab per enabled direction: y = sum_d u_d * h_d */

@@ -4,6 +4,7 @@
     gx, gw_raw, glam, gu = scan_bwd(x, w_raw, lam, u, gy, dirs=15, groups=1, ch_per_weight=1)
     y = scan_fwd_dirs(x, w_raw, lam_d, u_d, ...)   # per-direction gains / gates
     ys = scan_fwd_batched([dict(x=..., w_raw=..., lam=..., u=...), ...])   # one launch
+    y = gspn_scan(x, w_raw, lam, u, ...)   # differentiable: autograd runs scan_bwd
 
 computes the 4-direction line recurrence of the Generalized Spatial
 Propagation Network with hand-written HIP kernels (libgspn.so, C ABI in
@@ -20,7 +21,7 @@ from . import _lib
 from ._lib import (DIR_ALL, DIR_BT, DIR_LR, DIR_RL, DIR_TB, PATH_AUTO, PATH_FUSED, PATH_GENERAL,
                    GspnError, load, select_path)
 
-__all__ = ["scan_fwd", "scan_bwd", "scan_fwd_dirs", "scan_bwd_dirs", "scan_fwd_batched", "select_path", "load", "GspnError", "DIR_TB", "DIR_BT", "DIR_LR", "DIR_RL",
+__all__ = ["scan_fwd", "scan_bwd", "scan_fwd_dirs", "scan_bwd_dirs", "scan_fwd_batched", "gspn_scan", "select_path", "load", "GspnError", "DIR_TB", "DIR_BT", "DIR_LR", "DIR_RL",
            "DIR_ALL", "PATH_AUTO", "PATH_FUSED", "PATH_GENERAL"]
 
 
@@ -175,6 +176,41 @@ def scan_bwd_dirs(x, w_raw, lam, u, gy, *, dirs: int = DIR_ALL, groups: int = 1,
                                   stream=stream)
     _lib.check(rc)
     return gx, gw, glam, gu
+
+
+def _autograd_function():
+    import torch
+
+    class _GspnScan(torch.autograd.Function):
+        """y = scan_fwd(...) with scan_bwd as its backward (both HIP)."""
+
+        @staticmethod
+        def forward(ctx, x, w_raw, lam, u, dirs, groups, ch_per_weight):
+            ctx.save_for_backward(x, w_raw, lam, u)
+            ctx.opts = (dirs, groups, ch_per_weight)
+            return scan_fwd(x, w_raw, lam, u, dirs=dirs, groups=groups, ch_per_weight=ch_per_weight)
+
+        @staticmethod
+        def backward(ctx, gy):
+            x, w_raw, lam, u = ctx.saved_tensors
+            dirs, groups, ch_per_weight = ctx.opts
+            gx, gw, glam, gu = scan_bwd(x, w_raw, lam, u, gy.contiguous(), dirs=dirs, groups=groups,
+                                        ch_per_weight=ch_per_weight)
+            return gx, gw, glam, gu, None, None, None
+
+    return _GspnScan
+
+
+_GSPN_SCAN = None
+
+
+def gspn_scan(x, w_raw, lam, u, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1):
+    """scan_fwd as a differentiable torch operation: autograd calls scan_bwd
+    (the HIP backward) for the gradients of x, w_raw, lam and u."""
+    global _GSPN_SCAN
+    if _GSPN_SCAN is None:
+        _GSPN_SCAN = _autograd_function()
+    return _GSPN_SCAN.apply(x, w_raw, lam, u, dirs, groups, ch_per_weight)
 
 
 def scan_fwd_batched(problems):

@@ -200,3 +200,22 @@ def test_bwd_unread_taps_are_ignored_and_get_zero():
     gw = dirty[1]
     assert not gw[0, :, :, :, ::L_r].any() and not gw[2, :, :, :, :, ::L_c].any()
     assert not gw[0:2, :, :, 0, :, 0].any() and not gw[2:4, :, :, 2, H - 1, :].any()
+
+
+def test_autograd_wrapper_gives_the_backward_gradients():
+    """gspn_scan under autograd: the gradients of sum(y * gy) are exactly
+    scan_bwd's outputs (the same kernels), and y is scan_fwd's."""
+    import torch
+    import linear_spatial_propagation_amd as gspn
+    wl = make_workload(2, 8, 40, 48, groups=2, cpw=4, dtype="bf16", seed=61)
+    gy = to_device(make_gy(wl, 62), "bf16")
+    leaves = [to_device(a, "bf16").requires_grad_() for a in (wl.x_store, wl.w_store, wl.lam_store, wl.u_store)]
+    y = gspn.gspn_scan(*leaves, groups=2, ch_per_weight=4)
+    (y.float() * gy.float()).sum().backward()
+    plain = [t.detach() for t in leaves]
+    y_ref = gspn.scan_fwd(*plain, groups=2, ch_per_weight=4)
+    want = gspn.scan_bwd(*plain, gy, groups=2, ch_per_weight=4)
+    torch.cuda.synchronize()
+    assert torch.equal(y.detach(), y_ref)
+    for leaf, w in zip(leaves, want):
+        assert torch.equal(leaf.grad, w)
