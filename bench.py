@@ -484,7 +484,7 @@ def main():
     # practical ceiling, for context: a plain device-to-device copy of
     # 2 x 512 MiB buffers (read + write bytes per second), median of 20
     copy_gbps = None
-    if batched == 1:
+    if batched == 1 and not args.copy_calibration:   # the counter runs keep one known copy
         csrc = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
         cdst = torch.empty_like(csrc)
         cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]

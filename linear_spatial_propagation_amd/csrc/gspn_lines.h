@@ -359,6 +359,15 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams prm) {
 
     if (r0 + kTile <= H && c0 + kTile <= W && W % 16 == 0 && H % 16 == 0) {
         const int i = threadIdx.x >> 2, j0 = (threadIdx.x & 3) * 16;   // tile row i, columns j0..j0+15
+        const size_t o = (size_t)(r0 + i) * W + c0 + j0;
+        constexpr int N = 16 / (int)sizeof(T);
+        // the multipliers are loaded first: their latency overlaps the
+        // plane reads and the transpose instead of following the barrier
+        uint4 gv[NP][16 / N];
+#pragma unroll
+        for (int j = 0; j < NP; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; e += N) gv[j][e / N] = *reinterpret_cast<const uint4*>(gin[j] + o + e);
         float acc[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
@@ -391,17 +400,15 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams prm) {
             }
         }
         __syncthreads();
-        const size_t o = (size_t)(r0 + i) * W + c0 + j0;
         float sum[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) sum[e] = any_col ? acc[e] + tile[j0 + e][i] : acc[e];
-        constexpr int N = 16 / (int)sizeof(T);
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
 #pragma unroll
             for (int e = 0; e < 16; e += N) {
                 float f[N];
-                unpack(*reinterpret_cast<const uint4*>(gin[j] + o + e), f);
+                unpack(gv[j][e / N], f);
 #pragma unroll
                 for (int q = 0; q < N; ++q) f[q] *= sum[e + q];
                 store16_nt(gout[j] + o + e, f);   // not read again: non-temporal
