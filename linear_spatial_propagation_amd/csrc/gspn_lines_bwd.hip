@@ -27,12 +27,15 @@
 //     channels of a chunk of the set run in lockstep, so each pixel's taps
 //     are normalised once for all of them and their tap gradients are summed
 //     in registers.  g overwrites h in the planes (line i's slot is free once
-//     line i+1 has used h_i); dL/da goes to an fp32 workspace, line-major.
-//     Sets with more channels than one chunk take one launch per chunk, the
-//     later ones adding to the workspace;
+//     line i+1 has used h_i).  When a set's channels fit one chunk, dL/da
+//     is rounded to the storage dtype in this kernel: the row directions
+//     write the caller's tensor, the column directions a line-major copy.
+//     Otherwise it goes to an fp32 workspace, line-major, one launch per
+//     chunk, the later ones adding to it;
 //  5. merge_kernel: gx = lam * G, glam = x * G;
-//  6. the tap gradients to the caller's layout and dtype (transposed back for
-//     LR / RL).
+//  6. the tap gradients to the caller's layout and dtype: a transpose of the
+//     column directions' copies (and, from the fp32 workspace, a conversion
+//     of the row directions').
 #include "gspn_lines.h"
 
 namespace gspn {
@@ -48,6 +51,7 @@ struct AdjointParams {
     const void* wT;     // [ncol][B][Cw][3][W][H]
     float* planes;      // [nd][B][C][n][m]: h on entry, the adjoint g on exit
     float* ga;          // [nd][B][Cw][3][n][m]: dL/d raw taps, line-major
+    void* gw_out;       // DIRECT: the caller's tap gradients, written by the row directions
     float* sink;        // absorbs the stores of idle lanes and finished steps
     int B, C, H, W, Cw, cpw, groups, nd;
     int chunk;          // this launch runs channels chunk*CH .. chunk*CH+CH-1 of every set
@@ -72,6 +76,26 @@ __device__ __forceinline__ void load_f32(float (&dst)[K], const float* p) {
 }
 
 template <int K>
+__device__ __forceinline__ void store_f32(float* p, const float (&v)[K]);
+
+// K values rounded to the storage dtype (round to nearest even) and stored.
+template <typename T, int K>
+__device__ __forceinline__ void store_t(T* p, const float (&v)[K]) {
+    if constexpr (sizeof(T) == 4) {
+        store_f32<K>(reinterpret_cast<float*>(p), v);
+    } else if constexpr (K == 1) {
+        *p = from_f32(v[0], (T*)nullptr);
+    } else if constexpr (K == 2) {
+        *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v[0], v[1]);
+    } else if constexpr (K == 4) {
+        *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    } else {
+        *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    }
+}
+
+template <int K>
 __device__ __forceinline__ void store_f32(float* p, const float (&v)[K]) {
     if constexpr (K == 1) {
         p[0] = v[0];
@@ -92,7 +116,11 @@ struct AdjointStep {
     float gp[ACC ? 3 : 1][K];    // earlier chunks' dL/da at line i (ACC only)
 };
 
-template <typename T, int K, int CH, bool ACC>
+// DIRECT (a set's channels in one chunk, so nothing accumulates across
+// launches): the tap gradients are rounded to the storage dtype here; row
+// directions write the caller's layout, column directions a line-major
+// workspace that one transpose puts in place.
+template <typename T, int K, int CH, bool ACC, bool DIRECT>
 __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
     const int lane = threadIdx.x & 63;
     const int unit = blockIdx.x * 4 + uniform(threadIdx.x >> 6);   // (slot, b, k), k fastest
@@ -297,9 +325,18 @@ __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
 #pragma unroll
                     for (int e = 0; e < K; ++e) ga[t][e] += q.gp[t][e];
             }
+            if constexpr (DIRECT) {
+                T* gt = (is_row ? static_cast<T*>(prm.gw_out) : reinterpret_cast<T*>(prm.ga)) +
+                        ((size_t)(slot * B + b) * Cw + k) * 3 * HW;
 #pragma unroll
-            for (int t = 0; t < 3; ++t)
-                store_f32<K>(put ? gas + t * HW + (size_t)j * m + p0 : prm.sink + K * lane, ga[t]);
+                for (int t = 0; t < 3; ++t)
+                    store_t<T, K>(put ? gt + t * HW + (size_t)j * m + p0 : reinterpret_cast<T*>(prm.sink) + K * lane,
+                                  ga[t]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+                    store_f32<K>(put ? gas + t * HW + (size_t)j * m + p0 : prm.sink + K * lane, ga[t]);
+            }
             // refill the slot with the step kDepth ahead (clamped), after use
             load_step(buf[s], max(i - kDepth, 0));
         }
@@ -332,14 +369,16 @@ __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ 
 }
 
 template <typename T>
-void launch_adjoint(const AdjointParams& p, int K, int CH, bool acc, hipStream_t stream) {
+void launch_adjoint(const AdjointParams& p, int K, int CH, bool acc, bool direct, hipStream_t stream) {
     const long units = (long)p.nd * p.B * p.Cw;
     const dim3 grid((unsigned)((units + 3) / 4)), block(256);
-#define GSPN_ADJ(KK, CC)                                                                                      \
-    if (K == KK && CH == CC) {                                                                                \
-        if (acc) hipLaunchKernelGGL((adjoint_scan_kernel<T, KK, CC, true>), grid, block, 0, stream, p);       \
-        else hipLaunchKernelGGL((adjoint_scan_kernel<T, KK, CC, false>), grid, block, 0, stream, p);          \
-        return;                                                                                               \
+#define GSPN_ADJ(KK, CC)                                                                                       \
+    if (K == KK && CH == CC) {                                                                                 \
+        if (acc) hipLaunchKernelGGL((adjoint_scan_kernel<T, KK, CC, true, false>), grid, block, 0, stream, p); \
+        else if (direct)                                                                                       \
+            hipLaunchKernelGGL((adjoint_scan_kernel<T, KK, CC, false, true>), grid, block, 0, stream, p);      \
+        else hipLaunchKernelGGL((adjoint_scan_kernel<T, KK, CC, false, false>), grid, block, 0, stream, p);    \
+        return;                                                                                                \
     }
     GSPN_ADJ(1, 1) GSPN_ADJ(1, 2) GSPN_ADJ(1, 4) GSPN_ADJ(1, 8)
     GSPN_ADJ(2, 1) GSPN_ADJ(2, 2) GSPN_ADJ(2, 4)
@@ -456,15 +495,16 @@ hipError_t launch_lines_bwd_t(const GradArgs& g, void* workspace, hipStream_t st
     r.gy = g.gy; r.u = a.u; r.gyT = gyT; r.uT = uT; r.w = a.w; r.wT = wT;
     r.u_ds = a.u_dir ? E : 0;
     r.uT_ds = a.u_dir ? E : 0;
-    r.planes = planes; r.ga = ga; r.sink = sink;
+    r.planes = planes; r.ga = ga; r.sink = sink; r.gw_out = g.gw;
     r.B = a.B; r.C = a.C; r.H = H; r.W = W; r.Cw = Cw; r.cpw = a.cpw; r.groups = a.groups; r.nd = p.nd;
     for (int s = 0; s < 4; ++s) { r.dir_of_slot[s] = p.dir_of_slot[s]; r.col_index[s] = p.col_index[s]; }
     const int K = lines_positions_per_lane(H, W);
     int CH = 8 / K;
     while (a.cpw % CH) CH /= 2;
+    const bool direct = a.cpw / CH == 1;   // one chunk: tap gradients rounded in the adjoint kernel
     for (int c = 0; c < a.cpw / CH; ++c) {
         r.chunk = c;
-        launch_adjoint<T>(r, K, CH, c > 0, stream);
+        launch_adjoint<T>(r, K, CH, c > 0, direct, stream);
     }
     // 5. gx = lam * G, glam = x * G; per-direction lambda:
     //    gx = sum_d lam_d * g_d, glam_d = x * g_d
@@ -481,9 +521,16 @@ hipError_t launch_lines_bwd_t(const GradArgs& g, void* workspace, hipStream_t st
         q.in[0] = a.lam; q.out[0] = g.gx; q.in[1] = a.x; q.out[1] = g.glam;
         launch_merge<T, 2>(q, stream);
     }
-    // 6. tap gradients in the caller's layout and dtype
+    // 6. tap gradients in the caller's layout and dtype (direct: only the
+    //    column directions' line-major copies remain to be transposed)
     const size_t slab = wslab * HW;
     for (int s = 0; s < p.nd; ++s) {
+        if (direct) {
+            if (p.dir_of_slot[s] >= 2)
+                launch_transpose(reinterpret_cast<const T*>(ga) + (size_t)s * slab, static_cast<T*>(g.gw) + (size_t)s * slab,
+                                 wslab, W, H, stream);
+            continue;
+        }
         const float* src = ga + (size_t)s * slab;
         T* dst = static_cast<T*>(g.gw) + (size_t)s * slab;
         if (p.dir_of_slot[s] >= 2) {
