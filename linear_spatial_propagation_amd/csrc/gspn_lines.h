@@ -170,12 +170,14 @@ struct LineData {
 template <typename T, int K, int D>
 __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
     const int lane = threadIdx.x & 63;
-    const int unit = blockIdx.x * 4 + uniform(threadIdx.x >> 6);   // (slot, b, c), c fastest
+    const int unit = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
     const int C = prm.C, B = prm.B;
     if (unit >= prm.nd * B * C) return;   // whole wave
-    const int c = unit % C;
-    const int b = (unit / C) % B;
-    const int slot = unit / (C * B);
+    // (b, c, slot), slot fastest: the directions of one slice run side by
+    // side, so the pair that reads the same x and lambda shares them in cache
+    const int slot = unit % prm.nd;
+    const int c = (unit / prm.nd) % C;
+    const int b = unit / (prm.nd * C);
     const int d = prm.dir_of_slot[slot];
     const int k = c / prm.cpw;
     const bool is_row = d < 2;

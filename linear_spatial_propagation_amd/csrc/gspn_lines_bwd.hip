@@ -123,12 +123,14 @@ struct AdjointStep {
 template <typename T, int K, int CH, bool ACC, bool DIRECT>
 __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
     const int lane = threadIdx.x & 63;
-    const int unit = blockIdx.x * 4 + uniform(threadIdx.x >> 6);   // (slot, b, k), k fastest
+    // (b, k, slot), slot fastest: the directions of one set run side by side,
+    // so the pair that reads the same gy and u shares them in cache
+    const int unit = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
     const int B = prm.B, C = prm.C, Cw = prm.Cw;
     if (unit >= prm.nd * B * Cw) return;   // whole wave
-    const int k = unit % Cw;
-    const int b = (unit / Cw) % B;
-    const int slot = unit / (Cw * B);
+    const int slot = unit % prm.nd;
+    const int k = (unit / prm.nd) % Cw;
+    const int b = unit / (prm.nd * Cw);
     const int d = prm.dir_of_slot[slot];
     const bool is_row = d < 2;
     const bool asc = d == 0 || d == 2;
