@@ -167,10 +167,15 @@ struct LineData {
 
 // D: lines loaded ahead (deeper for long lines: fewer waves share the GPU
 // then, so each must keep more bytes in flight).
-template <typename T, int K, int D>
+// SPLIT = 2: a line is held by the two waves of a 128-thread workgroup, each
+// owning 64 K consecutive positions; after every line they swap the state at
+// their common edge through LDS (one barrier per line).  Halving the unit of
+// work balances launches whose scans barely exceed one wave per SIMD.
+template <typename T, int K, int D, int SPLIT>
 __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
     const int lane = threadIdx.x & 63;
-    const int unit = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+    const int half = SPLIT == 2 ? uniform(threadIdx.x >> 6) : 0;   // which part of the line
+    const int unit = SPLIT == 2 ? (int)blockIdx.x : (int)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
     const int C = prm.C, B = prm.B;
     if (unit >= prm.nd * B * C) return;   // whole wave
     // (b, c, slot), slot fastest: the directions of one slice run side by
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
     // compiler cannot see through, so that it stays branch-free (a select
     // on loaded data turned into exec-masked branches with conservative
     // memory-counter waits).
-    const int p0 = K * lane;
+    const int p0 = half * 64 * K + K * lane;
     const bool lane_on = p0 < m;
     const int pl = lane_on ? p0 : m - K;   // clamped (m % K == 0, m >= K)
     auto opaque = [](bool on) {
@@ -236,6 +241,12 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
     float h[K];
 #pragma unroll
     for (int e = 0; e < K; ++e) h[e] = 0.0f;
+    // SPLIT: the neighbour part's state at the common edge (position
+    // 64K - 1 or 64K of the line), from the previous line
+    __shared__ float edge[2][2];   // [line parity][part]
+    float bnd = 0.0f;
+    const bool takes_left = SPLIT == 2 && half == 1 && lane == 0;
+    const bool takes_right = SPLIT == 2 && half == 0 && lane == 63;
 
     // D lines per iteration; steps past the last line (when D does not
     // divide n) compute on clamped data and store nothing
@@ -283,8 +294,16 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
                         w2[e] = tp.w2;
                     }
                 }
-                const float left = from_left(h[K - 1]);
-                const float right = from_right(h[0]);
+                float left = from_left(h[K - 1]);
+                float right = from_right(h[0]);
+                if constexpr (SPLIT == 2) {
+                    // the lane exchange runs in every lane before the edge
+                    // lanes take the other part's value: sunk into a branch
+                    // it would read the masked-off edge lanes as 0
+                    asm volatile("" : "+v"(left), "+v"(right));
+                    left = takes_left ? bnd : left;
+                    right = takes_right ? bnd : right;
+                }
 #pragma unroll
                 for (int e = 0; e < K; ++e) {
                     const float hl = e == 0 ? left : h[e - 1];
@@ -296,6 +315,16 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
             }
 #pragma unroll
             for (int e = 0; e < K; ++e) h[e] = hn[e];
+            if constexpr (SPLIT == 2) {
+                // swap the edge states; the parity double-buffers the slots so
+                // that one barrier per line suffices
+                const int par = i & 1;
+                if (lane == (half == 0 ? 63 : 0)) edge[par][half] = half == 0 ? h[K - 1] : h[0];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+                bnd = edge[par][half ^ 1];
+            }
             {
                 // unconditional store (a store under a divergent branch also
                 // makes the counter waits conservative): lanes past the line
@@ -599,10 +628,11 @@ void launch_line_scan(const LineParams& p, hipStream_t stream) {
     const long units = (long)p.nd * p.B * p.C;
     const dim3 grid((unsigned)((units + 3) / 4));
     const int m = p.H > p.W ? p.H : p.W;
-    if (m <= 64) hipLaunchKernelGGL((line_scan_kernel<T, 1, kDepth>), grid, dim3(256), 0, stream, p);
-    else if (m <= 128) hipLaunchKernelGGL((line_scan_kernel<T, 2, kDepth>), grid, dim3(256), 0, stream, p);
-    else if (m <= 256) hipLaunchKernelGGL((line_scan_kernel<T, 4, kDepthK4>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((line_scan_kernel<T, 8, kDepth>), grid, dim3(256), 0, stream, p);
+    if (m <= 64) hipLaunchKernelGGL((line_scan_kernel<T, 1, kDepth, 1>), grid, dim3(256), 0, stream, p);
+    else if (m <= 128) hipLaunchKernelGGL((line_scan_kernel<T, 2, kDepth, 1>), grid, dim3(256), 0, stream, p);
+    else if (m <= 256) hipLaunchKernelGGL((line_scan_kernel<T, 4, kDepthK4, 1>), grid, dim3(256), 0, stream, p);
+    else   // sides above 256: two waves of 4 positions per lane hold a line
+        hipLaunchKernelGGL((line_scan_kernel<T, 4, kDepthK4, 2>), dim3((unsigned)units), dim3(128), 0, stream, p);
 }
 
 template <typename T>
