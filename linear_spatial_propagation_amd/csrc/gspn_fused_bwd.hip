@@ -43,6 +43,10 @@ constexpr int kBPitch = kBS + 3;
 constexpr int kBPlane = (kBS + 2) * kBPitch;
 constexpr int kBThreads = 256;
 constexpr int kBDepth = 4;           // LDS reads issued this many steps ahead
+// Pitch of the [slot][position] arrays of the prologue and epilogue (sigmoid
+// sums, exchange area): a multiple of 4 that is not one of 64, so that 16-byte
+// accesses by lanes holding consecutive slots fall into distinct banks.
+constexpr int kXP = kBS + 4;
 
 struct FusedBwdParams {
     const void* x;
@@ -192,7 +196,7 @@ void fused_bwd_kernel(FusedBwdParams prm) {
     // LDS: GH | HP[4] (channel loop) | SG[4] (sigmoid sums, [slot][position]
     // per direction).  The prologue's exact-form branch borrows 4096 floats
     // per wave of the channel-loop planes before they are zeroed.
-    constexpr int kSG = kBS * kBS;
+    constexpr int kSG = kBS * kXP;
     constexpr int kLoop = (5 * kBPlane + 3) / 4 * 4;     // channel-loop planes, padded
     __shared__ __attribute__((aligned(16))) float lds[kLoop + 4 * kSG];
     float* const GH = lds;
@@ -216,10 +220,14 @@ void fused_bwd_kernel(FusedBwdParams prm) {
     const int L = n / prm.groups;
     const bool has0 = p >= 1 && p < m;
     const bool has2 = p + 1 < m;
-    float* const SG = lds + kLoop + d * kSG + p;   // this wave's sums, [slot * 64]
+    float* const SGw = lds + kLoop + d * kSG;      // this wave's sums, [slot][position]
+    float* const SG = SGw + p;
     // per-wave exchange area for one chunk of per-slot registers (prologue
     // and epilogue only; it lies in the channel-loop planes): [value][slot]
-    float* const XR = lds + d * 4 * 16 * kBS + p;
+    // [position]
+    static_assert(4 * 4 * 16 * kXP <= kLoop, "exchange areas exceed the channel-loop planes");
+    float* const XRw = lds + d * 4 * 16 * kXP;
+    float* const XR = XRw + p;
 
     // slot t <-> line coordinate j
     auto line_of = [&](int t) { return asc ? t : kBS - 1 - t; };
@@ -311,6 +319,41 @@ void fused_bwd_kernel(FusedBwdParams prm) {
 #pragma unroll
             for (int t = 0; t < 3; ++t) a[t][i] = __uint_as_float(bits[t][i] & msk[i]);
     };
+    // Row directions with whole-vector rows take a chunk transposed: lane p
+    // holds slot t0 + (p & 15) at the 16 positions from 16 (p >> 4), so that
+    // its taps are read and written as 16-byte row vectors, and its entries
+    // of the [slot][position] arrays (exchange area, SG) are 16-byte vectors
+    // too (the pitch kXP keeps them free of bank conflicts).  Chunk values
+    // pass between the two layouts through the exchange area: a wave's LDS
+    // accesses complete in order.
+    const bool row_vec = VEC && is_row;
+    const int qi = p & (kChunk - 1);           // transposed: slot within the chunk
+    const int qpos = (p >> 4) * kChunk;        // transposed: first position
+    // taps of slot t0 + qi at positions qpos .. qpos+15 (0 outside the grid)
+    auto load_taps_rows = [&](int t0, float (&a)[3][kChunk]) __attribute__((always_inline)) {
+        const int j = line_of(t0 + qi);
+        uint4 raw[3][kNV];
+        uint32_t vm[kNV];
+#pragma unroll
+        for (int q = 0; q < kNV; ++q) {
+            const int cq = qpos + q * N;
+            const bool ok = j < n && cq < m;
+            vm[q] = opaque_mask(ok);
+            const size_t o = (size_t)min(j, n - 1) * W + (ok ? cq : 0);
+#pragma unroll
+            for (int u = 0; u < 3; ++u) raw[u][q] = *reinterpret_cast<const uint4*>(wd + (size_t)u * HW + o);
+        }
+#pragma unroll
+        for (int q = 0; q < kNV; ++q)
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                float f[N];
+                const uint4 r = raw[u][q];
+                unpack(make_uint4(r.x & vm[q], r.y & vm[q], r.z & vm[q], r.w & vm[q]), f);
+#pragma unroll
+                for (int e = 0; e < N; ++e) a[u][q * N + e] = f[e];
+            }
+    };
 
     // ---- normalised weights of every slot (0 where a slot reads no taps)
     // and the sum S of the sigmoids of its existing taps, kept for the
@@ -331,64 +374,78 @@ void fused_bwd_kernel(FusedBwdParams prm) {
     });
     if (on) {
         const float kNegLog2e = -1.44269504088896340736f;
-        for (int ch = 0; ch < kNCh; ++ch) {
-            const int t0 = ch * kChunk;
+        // One chunk in either layout.  Element e is slot t0 + e at position
+        // p, or (transposed) slot t0 + qi at position qpos + e; xo(e) is its
+        // entry in the exchange area.
+        auto norm_chunk = [&](int t0, auto tr_tag) __attribute__((always_inline)) {
+            constexpr bool TR = decltype(tr_tag)::value;
             float a[3][kChunk];
-            load_taps(t0, a);
+            if constexpr (TR) load_taps_rows(t0, a);
+            else load_taps(t0, a);
+            auto slot = [&](int e) { return TR ? t0 + qi : t0 + e; };
+            auto pos = [&](int e) { return TR ? qpos + e : p; };
+            auto xo = [&](int e) { return TR ? qi * kXP + qpos + e : e * kXP + p; };
             float amin = 0.0f;
 #pragma unroll
-            for (int i = 0; i < kChunk; ++i) {
-                const int t = t0 + i;
+            for (int e = 0; e < kChunk; ++e) {
+                const int t = slot(e), ps = pos(e);
                 const bool cpl = (coupled >> t) & 1u;
+                const bool h0 = ps >= 1 && ps < m, h2 = ps + 1 < m;
                 // unused taps (missing neighbours, unused lines) are taken as 0
-                const float a0 = cpl && has0 ? a[0][i] : 0.0f;
-                const float a1 = cpl ? a[1][i] : 0.0f;
-                const float a2 = cpl && has2 ? a[2][i] : 0.0f;
+                const float a0 = cpl && h0 ? a[0][e] : 0.0f;
+                const float a1 = cpl ? a[1][e] : 0.0f;
+                const float a2 = cpl && h2 ? a[2][e] : 0.0f;
                 amin = fminf(amin, fminf(fminf(a0, a1), a2));
                 const float q0 = 1.0f + fast_exp2(a0 * kNegLog2e);
                 const float q1 = 1.0f + fast_exp2(a1 * kNegLog2e);
                 const float q2 = 1.0f + fast_exp2(a2 * kNegLog2e);
-                const float p12 = has0 ? q1 * q2 : 0.0f;
-                const float p01 = has2 ? q0 * q1 : 0.0f;
+                const float p12 = h0 ? q1 * q2 : 0.0f;
+                const float p01 = h2 ? q0 * q1 : 0.0f;
                 const float D = fmaf(q0, q2, p12) + p01;
                 const float inv = fast_rcp(D);
-                XR[i * kBS] = cpl ? p12 * inv : 0.0f;
-                XR[(kChunk + i) * kBS] = cpl ? p01 * inv : 0.0f;
-                SG[t * kBS] = D * fast_rcp(q0 * q1 * q2);
+                XRw[xo(e)] = cpl ? p12 * inv : 0.0f;
+                XRw[kChunk * kXP + xo(e)] = cpl ? p01 * inv : 0.0f;
+                SGw[t * kXP + ps] = D * fast_rcp(q0 * q1 * q2);
             }
             if (__builtin_amdgcn_ballot_w64(amin < -25.0f) != 0) {
                 // exact form for this chunk
-                for (int i = 0; i < kChunk; ++i) {
-                    const int t = t0 + i;
+                for (int e = 0; e < kChunk; ++e) {
+                    const int t = slot(e), ps = pos(e);
                     const bool cpl = (coupled >> t) & 1u;
+                    const bool h0 = ps >= 1 && ps < m, h2 = ps + 1 < m;
                     float v3[3];
 #pragma unroll
                     for (int u = 0; u < 3; ++u) v3[u] = a[u][0];
 #pragma unroll
-                    for (int ii = 1; ii < kChunk; ++ii)   // a[.][i] without a dynamic index
-                        if (ii == i)
+                    for (int ee = 1; ee < kChunk; ++ee)   // a[.][e] without a dynamic index
+                        if (ee == e)
 #pragma unroll
-                            for (int u = 0; u < 3; ++u) v3[u] = a[u][ii];
-                    const float a0 = cpl && has0 ? v3[0] : 0.0f;
+                            for (int u = 0; u < 3; ++u) v3[u] = a[u][ee];
+                    const float a0 = cpl && h0 ? v3[0] : 0.0f;
                     const float a1 = cpl ? v3[1] : 0.0f;
-                    const float a2 = cpl && has2 ? v3[2] : 0.0f;
-                    const Taps tp = normalise_taps(a0, a1, a2, has0, has2);
-                    const float s0 = has0 ? fast_rcp(1.0f + fast_exp2(a0 * kNegLog2e)) : 0.0f;
+                    const float a2 = cpl && h2 ? v3[2] : 0.0f;
+                    const Taps tp = normalise_taps(a0, a1, a2, h0, h2);
+                    const float s0 = h0 ? fast_rcp(1.0f + fast_exp2(a0 * kNegLog2e)) : 0.0f;
                     const float s1 = fast_rcp(1.0f + fast_exp2(a1 * kNegLog2e));
-                    const float s2 = has2 ? fast_rcp(1.0f + fast_exp2(a2 * kNegLog2e)) : 0.0f;
-                    SG[t * kBS] = (s0 + s1) + s2;
-                    XR[i * kBS] = cpl ? tp.w0 : 0.0f;
-                    XR[(kChunk + i) * kBS] = cpl ? tp.w2 : 0.0f;
+                    const float s2 = h2 ? fast_rcp(1.0f + fast_exp2(a2 * kNegLog2e)) : 0.0f;
+                    SGw[t * kXP + ps] = (s0 + s1) + s2;
+                    XRw[xo(e)] = cpl ? tp.w0 : 0.0f;
+                    XRw[kChunk * kXP + xo(e)] = cpl ? tp.w2 : 0.0f;
                 }
             }
+        };
+        for (int ch = 0; ch < kNCh; ++ch) {
+            if (row_vec) norm_chunk(ch * kChunk, std::integral_constant<bool, true>{});
+            else norm_chunk(ch * kChunk, std::integral_constant<bool, false>{});
+            asm volatile("" ::: "memory");   // other lanes' entries (transposed chunks)
             // the chunk's weights into registers (one static block per chunk)
             switch (ch) {
 #define GSPN_UNDUMP(CH)                                                     \
                 case CH:                                                    \
                     sfor<0, kChunk>([&](auto ic) {                          \
                         constexpr int i = decltype(ic)::value;              \
-                        w0[CH * kChunk + i] = XR[i * kBS];                  \
-                        w2[CH * kChunk + i] = XR[(kChunk + i) * kBS];       \
+                        w0[CH * kChunk + i] = XR[i * kXP];                  \
+                        w2[CH * kChunk + i] = XR[(kChunk + i) * kXP];       \
                     });                                                     \
                     break;
                 GSPN_UNDUMP(0) GSPN_UNDUMP(1) GSPN_UNDUMP(2) GSPN_UNDUMP(3)
@@ -550,88 +607,123 @@ void fused_bwd_kernel(FusedBwdParams prm) {
     // and ga_t = w_t (1 - s_t) (D_t - sum_v w_v D_v).  Every weight is
     // formed directly (w1 = s1 / S), and 1 - s_t without cancellation:
     // 1 - s_t for s_t < 1/2, else exp(-a_t) s_t, with s_t = w_t S; so the raw
-    // taps are read again.  Loop over chunks of 16 slots, as the prologue.
+    // taps are read again.  The chunks of 16 slots run unrolled.
     if (on) {
         T* gwd = static_cast<T*>(prm.gw) + ((size_t)(slab * B + b) * Cw + k) * 3 * (size_t)HW;
         const float kNegLog2e = -1.44269504088896340736f;
-        for (int ch = 0; ch < kNCh; ++ch) {
-            const int t0 = ch * kChunk;
-            float a[3][kChunk];
-            load_taps(t0, a);
-            // the chunk's registers into LDS (one static block per chunk)
-            switch (ch) {
-#define GSPN_DUMP(CH)                                                       \
-                case CH:                                                    \
-                    sfor<0, kChunk>([&](auto ic) {                          \
-                        constexpr int i = decltype(ic)::value;              \
-                        XR[i * kBS] = w0[CH * kChunk + i];                  \
-                        XR[(kChunk + i) * kBS] = w2[CH * kChunk + i];       \
-                        XR[(2 * kChunk + i) * kBS] = e0[CH * kChunk + i];   \
-                        XR[(3 * kChunk + i) * kBS] = e2[CH * kChunk + i];   \
-                    });                                                     \
-                    break;
-                GSPN_DUMP(0) GSPN_DUMP(1) GSPN_DUMP(2) GSPN_DUMP(3)
-#undef GSPN_DUMP
-            }
-            float gaf[3][kChunk];
+        // tap gradients of one pixel: raw taps a3 (used where cpl and the
+        // neighbour exists), weights x0, x2, tap sums E0, E2, sigmoid sum S
+        auto tap_grads = [&](bool cpl, bool h0, bool h2, const float (&a3)[3], float x0, float x2, float E0,
+                             float E2, float S, float (&ga)[3]) __attribute__((always_inline)) {
+            const float av[3] = {cpl && h0 ? a3[0] : 0.0f, cpl ? a3[1] : 0.0f, cpl && h2 ? a3[2] : 0.0f};
+            float ex[3];
 #pragma unroll
-            for (int i = 0; i < kChunk; ++i) {
-                const int t = t0 + i;
+            for (int u = 0; u < 3; ++u) ex[u] = fast_exp2(av[u] * kNegLog2e);   // may be inf
+            // w1 = sigmoid(a1) / S; if every sigmoid underflows, the
+            // weights came from the exact form and w1 = 1 - w0 - w2
+            const float w1d = fast_rcp(1.0f + ex[1]) * fast_rcp(S);
+            const float wv[3] = {x0, S > 1e-30f ? w1d : 1.0f - x0 - x2, x2};
+            float om[3];
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                const float sg = wv[u] * S;
+                om[u] = sg < 0.5f ? 1.0f - sg : ex[u] * sg;
+            }
+            const float r0 = fmaf(wv[1], E0, wv[2] * (E0 - E2));
+            const float r1 = -fmaf(wv[0], E0, wv[2] * E2);
+            const float r2 = fmaf(wv[1], E2, wv[0] * (E2 - E0));
+            ga[0] = cpl ? wv[0] * om[0] * r0 : 0.0f;
+            ga[1] = cpl ? wv[1] * om[1] * r1 : 0.0f;
+            ga[2] = cpl ? wv[2] * om[2] * r2 : 0.0f;
+        };
+        sfor<0, kNCh>([&](auto cc) {
+            constexpr int ch = decltype(cc)::value;
+            constexpr int t0 = ch * kChunk;
+            // the chunk's registers into LDS
+            sfor<0, kChunk>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                XR[i * kXP] = w0[ch * kChunk + i];
+                XR[(kChunk + i) * kXP] = w2[ch * kChunk + i];
+                XR[(2 * kChunk + i) * kXP] = e0[ch * kChunk + i];
+                XR[(3 * kChunk + i) * kXP] = e2[ch * kChunk + i];
+            });
+            if (row_vec) {
+                asm volatile("" ::: "memory");   // other lanes' entries
+                const int t = t0 + qi;
+                const int j = line_of(t);
                 const bool cpl = (coupled >> t) & 1u;
-                const float S = SG[t * kBS];
-                const float x0 = XR[i * kBS], x2 = XR[(kChunk + i) * kBS];
-                const float E0 = XR[(2 * kChunk + i) * kBS], E2 = XR[(3 * kChunk + i) * kBS];
-                const float av[3] = {cpl && has0 ? a[0][i] : 0.0f, cpl ? a[1][i] : 0.0f,
-                                     cpl && has2 ? a[2][i] : 0.0f};
-                float ex[3];
+                float a[3][kChunk];
+                load_taps_rows(t0, a);
+                const float* xr = XRw + qi * kXP + qpos;
+                const float* sg = SGw + t * kXP + qpos;
+                float gaf[3][kChunk];
 #pragma unroll
-                for (int u = 0; u < 3; ++u) ex[u] = fast_exp2(av[u] * kNegLog2e);   // may be inf
-                // w1 = sigmoid(a1) / S; if every sigmoid underflows, the
-                // weights came from the exact form and w1 = 1 - w0 - w2
-                const float w1d = fast_rcp(1.0f + ex[1]) * fast_rcp(S);
-                const float wv[3] = {x0, S > 1e-30f ? w1d : 1.0f - x0 - x2, x2};
-                float om[3];
+                for (int e = 0; e < kChunk; ++e) {
+                    const int pos = qpos + e;
+                    const float a3[3] = {a[0][e], a[1][e], a[2][e]};
+                    float ga[3];
+                    tap_grads(cpl, pos >= 1 && pos < m, pos + 1 < m, a3, xr[e], xr[kChunk * kXP + e],
+                              xr[2 * kChunk * kXP + e], xr[3 * kChunk * kXP + e], sg[e], ga);
 #pragma unroll
-                for (int u = 0; u < 3; ++u) {
-                    const float sg = wv[u] * S;
-                    om[u] = sg < 0.5f ? 1.0f - sg : ex[u] * sg;
+                    for (int u = 0; u < 3; ++u) gaf[u][e] = ga[u];
                 }
-                const float r0 = fmaf(wv[1], E0, wv[2] * (E0 - E2));
-                const float r1 = -fmaf(wv[0], E0, wv[2] * E2);
-                const float r2 = fmaf(wv[1], E2, wv[0] * (E2 - E0));
-                gaf[0][i] = cpl ? wv[0] * om[0] * r0 : 0.0f;
-                gaf[1][i] = cpl ? wv[1] * om[1] * r1 : 0.0f;
-                gaf[2][i] = cpl ? wv[2] * om[2] * r2 : 0.0f;
-            }
-            if (col_vec) {
-                // lane p writes its row: the chunk's columns as 16-byte vectors
-                const int c0 = chunk_col0(t0);
 #pragma unroll
                 for (int q = 0; q < kNV; ++q) {
-                    const int cq = c0 + q * N;
-                    if (cq < n && p < m) {
+                    const int cq = qpos + q * N;
+                    if (j < n && cq < m) {
 #pragma unroll
                         for (int u = 0; u < 3; ++u) {
                             float f[N];
 #pragma unroll
-                            for (int e = 0; e < N; ++e)
-                                f[e] = asc ? gaf[u][q * N + e] : gaf[u][kChunk - 1 - q * N - e];
-                            store16_nt(gwd + (size_t)u * HW + (size_t)p * W + cq, f);
+                            for (int e = 0; e < N; ++e) f[e] = gaf[u][q * N + e];
+                            store16(gwd + (size_t)u * HW + (size_t)j * W + cq, f);
                         }
                     }
                 }
             } else {
+                float a[3][kChunk];
+                load_taps(t0, a);
+                float gaf[3][kChunk];
 #pragma unroll
                 for (int i = 0; i < kChunk; ++i) {
-                    const int j = line_of(t0 + i);
-                    if (j < n && p < m) {
-                        const int o = pix(j, p);
+                    const int t = t0 + i;
+                    const float a3[3] = {a[0][i], a[1][i], a[2][i]};
+                    float ga[3];
+                    tap_grads((coupled >> t) & 1u, has0, has2, a3, XR[i * kXP], XR[(kChunk + i) * kXP],
+                              XR[(2 * kChunk + i) * kXP], XR[(3 * kChunk + i) * kXP], SG[t * kXP], ga);
 #pragma unroll
-                        for (int u = 0; u < 3; ++u) gwd[(size_t)u * HW + o] = from_f32(gaf[u][i], (T*)nullptr);
+                    for (int u = 0; u < 3; ++u) gaf[u][i] = ga[u];
+                }
+                if (col_vec) {
+                    // lane p writes its row: the chunk's columns as 16-byte vectors
+                    const int c0 = chunk_col0(t0);
+#pragma unroll
+                    for (int q = 0; q < kNV; ++q) {
+                        const int cq = c0 + q * N;
+                        if (cq < n && p < m) {
+#pragma unroll
+                            for (int u = 0; u < 3; ++u) {
+                                float f[N];
+#pragma unroll
+                                for (int e = 0; e < N; ++e)
+                                    f[e] = asc ? gaf[u][q * N + e] : gaf[u][kChunk - 1 - q * N - e];
+                                store16(gwd + (size_t)u * HW + (size_t)p * W + cq, f);
+                            }
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < kChunk; ++i) {
+                        const int j = line_of(t0 + i);
+                        if (j < n && p < m) {
+                            const int o = pix(j, p);
+#pragma unroll
+                            for (int u = 0; u < 3; ++u) gwd[(size_t)u * HW + o] = from_f32(gaf[u][i], (T*)nullptr);
+                        }
                     }
                 }
             }
-        }
+        });
     }
 }
 

@@ -30,6 +30,14 @@ __device__ __forceinline__ void unpack(uint4 r, float (&o)[8]) {
 __device__ __forceinline__ void unpack(uint4 r, float (&o)[4]) {
     o[0] = __uint_as_float(r.x); o[1] = __uint_as_float(r.y); o[2] = __uint_as_float(r.z); o[3] = __uint_as_float(r.w);
 }
+// 16-byte store of 8 bf16 (rounded to nearest even) or 4 fp32
+__device__ __forceinline__ void store16(uint16_t* p, const float (&v)[8]) {
+    *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
+__device__ __forceinline__ void store16(float* p, const float (&v)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
 // non-temporal 16-byte store of 8 bf16 (rounded to nearest even) or 4 fp32
 __device__ __forceinline__ void store16_nt(uint16_t* p, const float (&v)[8]) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
