@@ -121,6 +121,9 @@ struct BwdDir {
 // Forward of one channel, in place: the plane P holds lam x on entry and h
 // on exit (slot t is read kBDepth steps before it is overwritten).
 //   h' = keep * (h + w0 (h[p-1] - h) + w2 (h[p+1] - h)) + lam x
+// KEEP = false when no slot after slot 0 starts a group: the state before
+// slot 0 is 0, so keep changes nothing there and the factor is left out.
+template <bool KEEP>
 __device__ __forceinline__ void fwd_scan(const BwdDir& v, float* P, const float (&w0)[kBS], const float (&w2)[kBS]) {
     // offsets advance by ds per slot; opaque here so that the compiler does
     // not hoist 64 precomputed offsets (or keep factors) out of the loop
@@ -138,12 +141,16 @@ __device__ __forceinline__ void fwd_scan(const BwdDir& v, float* P, const float 
         if constexpr (t + kBDepth < kBS) { xr[t % kBDepth] = P[ol]; ol += ds; }
         // keep the read issued here, kBDepth steps before its use
         __builtin_amdgcn_sched_barrier(0);
-        const float keep = ((st >> t) & 1u) ? 0.0f : 1.0f;
         const float dl = from_left(h) - h;
         const float dr = from_right(h) - h;
         float nv = fmaf(w0[t], dl, h);
         nv = fmaf(w2[t], dr, nv);
-        h = fmaf(keep, nv, xl);
+        if constexpr (KEEP) {
+            const float keep = ((st >> t) & 1u) ? 0.0f : 1.0f;
+            h = fmaf(keep, nv, xl);
+        } else {
+            h = nv + xl;
+        }
         P[o] = h;
         o += ds;
     });
@@ -153,6 +160,9 @@ __device__ __forceinline__ void fwd_scan(const BwdDir& v, float* P, const float 
 // exit: slot t's h is last read at slot t+1 (the step before), and the h of
 // slot t-1 is read kBDepth steps ahead, before slot t-1 is written.
 // E0 / E2 accumulate the tap-gradient differences of every slot.
+// KEEP = false when no slot after slot 0 starts a group: the carry out of
+// slot 0 is never used.
+template <bool KEEP>
 __device__ __forceinline__ void adj_scan(const BwdDir& v, const float* __restrict__ GH, float* __restrict__ P,
                                          const float (&w0)[kBS], const float (&w2)[kBS], float (&e0)[kBS],
                                          float (&e2)[kBS]) {
@@ -181,8 +191,11 @@ __device__ __forceinline__ void adj_scan(const BwdDir& v, const float* __restric
         e0[t] = fmaf(g, dl, e0[t]);
         e2[t] = fmaf(g, dr, e2[t]);
         const float c0 = w0[t] * g, c2 = w2[t] * g;
-        const float keep = ((st >> t) & 1u) ? 0.0f : 1.0f;
-        carry = keep * (((g - c0) - c2) + from_right(c0) + from_left(c2));
+        carry = ((g - c0) - c2) + from_right(c0) + from_left(c2);
+        if constexpr (KEEP) {
+            const float keep = ((st >> t) & 1u) ? 0.0f : 1.0f;
+            carry *= keep;
+        }
         P[o] = g;
         o -= ds;
     });
@@ -242,6 +255,10 @@ void fused_bwd_kernel(FusedBwdParams prm) {
         for (int s0 = 0; s0 < n; s0 += L) st |= 1ull << (asc ? s0 : s0 + kBS - n);
         v.starts = st;
     }
+    // a group starts after slot 0 (local groups, or BT / RL shorter than
+    // 64).  The fp32 instantiations always take the scans with the keep
+    // factor: a second copy of the scans costs them register spills.
+    const bool restarts = sizeof(T) == 4 || (v.starts & ~1ull) != 0;
     // slots whose line exists and reads the previous line (taps in use)
     uint64_t coupled = 0;
     for (int t = 0; t < kBS; ++t)
@@ -552,7 +569,10 @@ void fused_bwd_kernel(FusedBwdParams prm) {
         lds_barrier();
 
         // ---- forward: h of every direction into its plane
-        if (on) fwd_scan(v, Pd, w0, w2);
+        if (on) {
+            if (restarts) fwd_scan<true>(v, Pd, w0, w2);
+            else fwd_scan<false>(v, Pd, w0, w2);
+        }
         lds_barrier();
 
         // ---- gu = gy * sum_d h_d
@@ -570,7 +590,10 @@ void fused_bwd_kernel(FusedBwdParams prm) {
         lds_barrier();
 
         // ---- adjoint: g of every direction over its plane, tap sums
-        if (on) adj_scan(v, GH, Pd, w0, w2, e0, e2);
+        if (on) {
+            if (restarts) adj_scan<true>(v, GH, Pd, w0, w2, e0, e2);
+            else adj_scan<false>(v, GH, Pd, w0, w2, e0, e2);
+        }
         lds_barrier();
 
         // ---- gx = lam * G, glam = x * G
