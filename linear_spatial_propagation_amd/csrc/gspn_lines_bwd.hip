@@ -23,7 +23,8 @@
 //  2. line_scan_kernel: the forward again, h of every direction into fp32
 //     planes;
 //  3. merge_kernel: gu = gy * sum of the planes;
-//  4. adjoint_scan_kernel: one wave per (direction, b, weight set); the CH
+//  4. adjoint_scan_kernel: one wave per (direction, b, weight set), two for
+//     lines longer than 256; the CH
 //     channels of a chunk of the set run in lockstep, so each pixel's taps
 //     are normalised once for all of them and their tap gradients are summed
 //     in registers.  g overwrites h in the planes (line i's slot is free once
@@ -108,24 +109,32 @@ __device__ __forceinline__ void store_f32(float* p, const float (&v)[K]) {
 }
 
 // Everything one reverse step reads, for one lane.
-template <typename T, int K, int CH, bool ACC>
+template <typename T, int K, int CH, bool ACC, int SPLIT>
 struct AdjointStep {
     LineVec<T, K> a[3];          // raw taps of line i
     LineVec<T, K> gy[CH], u[CH]; // at line i
     float hp[CH][K];             // h_{i-1}
     float gp[ACC ? 3 : 1][K];    // earlier chunks' dL/da at line i (ACC only)
+    float hx[SPLIT == 2 ? CH : 1];   // SPLIT: h_{i-1} of the other part at the common edge
 };
 
 // DIRECT (a set's channels in one chunk, so nothing accumulates across
 // launches): the tap gradients are rounded to the storage dtype here; row
 // directions write the caller's layout, column directions a line-major
 // workspace that one transpose puts in place.
-template <typename T, int K, int CH, bool ACC, bool DIRECT>
+// SPLIT = 2 (CH = 1): a line is held by the two waves of a 128-thread
+// workgroup, each owning 64 K consecutive positions, as in the forward line
+// scan.  Each part reads the other's h_{i-1} at the common edge from the
+// planes, and after every step the two swap w0 g / w2 g at that edge through
+// LDS (one barrier per step).
+template <typename T, int K, int CH, bool ACC, bool DIRECT, int SPLIT>
 __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
+    static_assert(SPLIT == 1 || CH == 1, "split lines carry one channel");
     const int lane = threadIdx.x & 63;
+    const int half = SPLIT == 2 ? uniform(threadIdx.x >> 6) : 0;   // which part of the line
     // (b, k, slot), slot fastest: the directions of one set run side by side,
     // so the pair that reads the same gy and u shares them in cache
-    const int unit = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+    const int unit = SPLIT == 2 ? (int)blockIdx.x : (int)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
     const int B = prm.B, C = prm.C, Cw = prm.Cw;
     if (unit >= prm.nd * B * Cw) return;   // whole wave
     const int slot = unit % prm.nd;
@@ -155,7 +164,7 @@ __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
     // lane's positions p0 .. p0+K-1; lanes past the line read a clamped
     // vector and hold g = 0 (masks the compiler cannot see through keep the
     // code branch-free, as in the forward scan)
-    const int p0 = K * lane;
+    const int p0 = half * 64 * K + K * lane;
     const bool lane_on = p0 < m;
     const int pc = lane_on ? p0 : m - K;
     auto opaque = [](bool on) {
@@ -171,7 +180,12 @@ __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
     const float fl = lane_on ? 1.0f : 0.0f;
     auto masked = [](float v, uint32_t msk) { return __uint_as_float(__float_as_uint(v) & msk); };
 
-    using Step = AdjointStep<T, K, CH, ACC>;
+    using Step = AdjointStep<T, K, CH, ACC, SPLIT>;
+    // SPLIT: the lanes at the common edge and the other part's edge position
+    const bool takes_left = SPLIT == 2 && half == 1 && lane == 0;
+    const bool takes_right = SPLIT == 2 && half == 0 && lane == 63;
+    const int pe = min(half == 0 ? 64 * K : 64 * K - 1, m - 1);
+    __shared__ float xch[2][2];   // [step parity][part]: w2 g (part 0) / w0 g (part 1) at the edge
     auto load_step = [&](Step& q, int i) {   // 0 <= i < n
         const int j = asc ? i : n - 1 - i;
         const size_t o = (size_t)j * m + pc;
@@ -184,9 +198,14 @@ __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
             q.u[ch].load(us + ch * HW + o);
         }
         const int ip = i > 0 ? i - 1 : 0;
-        const size_t op = (size_t)(asc ? ip : n - 1 - ip) * m + pc;
+        const size_t lp = (size_t)(asc ? ip : n - 1 - ip) * m;
+        const size_t op = lp + pc;
 #pragma unroll
         for (int ch = 0; ch < CH; ++ch) load_f32<K>(q.hp[ch], pl + ch * HW + op);
+        if constexpr (SPLIT == 2) {
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch) q.hx[ch] = pl[ch * HW + lp + pe];
+        }
         if constexpr (ACC) {
 #pragma unroll
             for (int t = 0; t < 3; ++t) load_f32<K>(q.gp[t], gas + t * HW + o);
@@ -223,6 +242,7 @@ __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
             }
 
             float ga[3][K];
+            float cs0[SPLIT == 2 ? K : 1], cs2[SPLIT == 2 ? K : 1];   // SPLIT: w0 g, w2 g of line i
             if (coupled) {
                 // tap-gradient differences summed over the chunk's channels:
                 // E0 = sum g (h[p-1] - h[p]), E2 = sum g (h[p+1] - h[p])
@@ -231,8 +251,16 @@ __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
                 for (int e = 0; e < K; ++e) { ed[0][e] = 0.0f; ed[1][e] = 0.0f; }
 #pragma unroll
                 for (int ch = 0; ch < CH; ++ch) {
-                    const float left = from_left(q.hp[ch][K - 1]);
-                    const float right = from_right(q.hp[ch][0]);
+                    float left = from_left(q.hp[ch][K - 1]);
+                    float right = from_right(q.hp[ch][0]);
+                    if constexpr (SPLIT == 2) {
+                        // the lane exchange runs in every lane before the edge
+                        // lanes take the other part's value (sunk into a
+                        // branch it would read the masked-off lanes as 0)
+                        asm volatile("" : "+v"(left), "+v"(right));
+                        left = takes_left ? q.hx[ch] : left;
+                        right = takes_right ? q.hx[ch] : right;
+                    }
 #pragma unroll
                     for (int e = 0; e < K; ++e) {
                         const float hl = e == 0 ? left : q.hp[ch][e - 1];
@@ -294,7 +322,15 @@ __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
                     ga[2][e] = w2[e] * o2[e] * fmaf(w1[e], E2, w0[e] * (E2 - E0));
                 }
                 // carry into line i-1: (w_i^T g_i)[p] = w1 g[p] + w0[p+1] g[p+1]
-                // + w2[p-1] g[p-1], with w1 = 1 - w0 - w2
+                // + w2[p-1] g[p-1], with w1 = 1 - w0 - w2 (SPLIT: after the
+                // edge exchange below)
+                if constexpr (SPLIT == 2) {
+#pragma unroll
+                    for (int e = 0; e < K; ++e) {
+                        cs0[e] = w0[e] * g[0][e];
+                        cs2[e] = w2[e] * g[0][e];
+                    }
+                } else
 #pragma unroll
                 for (int ch = 0; ch < CH; ++ch) {
                     float c0[K], c2[K];
@@ -320,6 +356,31 @@ __global__ __launch_bounds__(256) void adjoint_scan_kernel(AdjointParams prm) {
                 for (int ch = 0; ch < CH; ++ch)
 #pragma unroll
                     for (int e = 0; e < K; ++e) carry[ch][e] = 0.0f;
+                if constexpr (SPLIT == 2) {
+#pragma unroll
+                    for (int e = 0; e < K; ++e) { cs0[e] = 0.0f; cs2[e] = 0.0f; }
+                }
+            }
+            if constexpr (SPLIT == 2) {
+                // swap w2 g / w0 g at the common edge; the step parity
+                // double-buffers the slots, so one barrier per step suffices
+                const int par = (s0 + s) & 1;
+                if (lane == (half == 0 ? 63 : 0)) xch[par][half] = half == 0 ? cs2[K - 1] : cs0[0];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+                const float xo = xch[par][half ^ 1];
+                float r0 = from_right(cs0[0]);
+                float l2 = from_left(cs2[K - 1]);
+                asm volatile("" : "+v"(r0), "+v"(l2));
+                r0 = takes_right ? xo : r0;
+                l2 = takes_left ? xo : l2;
+                if (coupled) {
+#pragma unroll
+                    for (int e = 0; e < K; ++e)
+                        carry[0][e] = (g[0][e] - cs0[e] - cs2[e]) + (e == K - 1 ? r0 : cs0[e + 1]) +
+                                      (e == 0 ? l2 : cs2[e - 1]);
+                }
             }
             if constexpr (ACC) {
 #pragma unroll
@@ -370,22 +431,31 @@ __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ 
     if (tid < count) dst[tid] = from_f32(src[tid], (T*)nullptr);
 }
 
+// Lines longer than 256 (K = 8) are split over two waves with 4 positions
+// each (the launch then has twice the waves, which balances scans that
+// barely exceed one wave per SIMD, as in the forward).
 template <typename T>
 void launch_adjoint(const AdjointParams& p, int K, int CH, bool acc, bool direct, hipStream_t stream) {
     const long units = (long)p.nd * p.B * p.Cw;
+    if (K == 8 && CH == 1) {
+        const dim3 grid((unsigned)units), block(128);
+        if (acc) hipLaunchKernelGGL((adjoint_scan_kernel<T, 4, 1, true, false, 2>), grid, block, 0, stream, p);
+        else if (direct) hipLaunchKernelGGL((adjoint_scan_kernel<T, 4, 1, false, true, 2>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((adjoint_scan_kernel<T, 4, 1, false, false, 2>), grid, block, 0, stream, p);
+        return;
+    }
     const dim3 grid((unsigned)((units + 3) / 4)), block(256);
-#define GSPN_ADJ(KK, CC)                                                                                       \
-    if (K == KK && CH == CC) {                                                                                 \
-        if (acc) hipLaunchKernelGGL((adjoint_scan_kernel<T, KK, CC, true, false>), grid, block, 0, stream, p); \
-        else if (direct)                                                                                       \
-            hipLaunchKernelGGL((adjoint_scan_kernel<T, KK, CC, false, true>), grid, block, 0, stream, p);      \
-        else hipLaunchKernelGGL((adjoint_scan_kernel<T, KK, CC, false, false>), grid, block, 0, stream, p);    \
-        return;                                                                                                \
+#define GSPN_ADJ(KK, CC)                                                                                          \
+    if (K == KK && CH == CC) {                                                                                    \
+        if (acc) hipLaunchKernelGGL((adjoint_scan_kernel<T, KK, CC, true, false, 1>), grid, block, 0, stream, p); \
+        else if (direct)                                                                                          \
+            hipLaunchKernelGGL((adjoint_scan_kernel<T, KK, CC, false, true, 1>), grid, block, 0, stream, p);      \
+        else hipLaunchKernelGGL((adjoint_scan_kernel<T, KK, CC, false, false, 1>), grid, block, 0, stream, p);    \
+        return;                                                                                                   \
     }
     GSPN_ADJ(1, 1) GSPN_ADJ(1, 2) GSPN_ADJ(1, 4) GSPN_ADJ(1, 8)
     GSPN_ADJ(2, 1) GSPN_ADJ(2, 2) GSPN_ADJ(2, 4)
     GSPN_ADJ(4, 1) GSPN_ADJ(4, 2)
-    GSPN_ADJ(8, 1)
 #undef GSPN_ADJ
 }
 

@@ -77,6 +77,9 @@ EDGE_BWD = [
     (1, 4, 128, 96, 12, 1, 4),    # column directions only
     (1, 3, 128, 64, 6, 4, 3),
     (1, 2, 512, 504, 15, 1, 2),   # K = 8, two chunks of one
+    (1, 2, 264, 272, 15, 4, 1),   # K = 8 (lines held by two waves), local groups
+    (1, 3, 512, 16, 15, 1, 3),    # K = 8, three chunks of one; row lines fit one wave
+    (2, 1, 264, 264, 5, 1, 1),    # K = 8, TB and LR only
 ]
 
 
