@@ -180,6 +180,63 @@ def scan_bwd_dirs(x, w, lam, u, gy, *, dirs: int = 15, groups: int = 1, cpw: int
     return gx, gw, glam, gu
 
 
+
+def round_bf16(a) -> np.ndarray:
+    """Values rounded to bfloat16 (round to nearest, ties to even), in fp64.
+
+    The fp64 value is first rounded to fp32 (numpy's conversion rounds to
+    nearest even), then its low 16 bits are rounded away, ties to even.
+    """
+    f = np.ascontiguousarray(a, dtype=np.float32)
+    b = f.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def block_rows(C_proxy: int, dirs: int, cpw: int) -> int:
+    """Rows of the block's input projection: proxy, taps, lambda, u."""
+    nd = bin(dirs & 15).count("1")
+    return C_proxy + nd * (C_proxy // cpw) * 3 + 2 * C_proxy
+
+
+def block_fwd(x, w_in, w_out, *, dirs: int = 15, groups: int = 1, cpw: int = 1, io_round=None,
+              nthreads: int = 0, lib=None) -> np.ndarray:
+    """The compressed propagation block around the scan, in fp64.
+
+    Reading of the block (GSPN-2 response, *Relate Compressive Proxy
+    Dimension to Low-rank Approximation*; C-GSPN abstract): per pixel, one
+    linear layer maps the C input channels to x_proxy (C_proxy channels),
+    the raw taps, lambda and u; the scan runs over x_proxy; a second linear
+    layer maps its C_proxy output channels back to C.
+
+    x: [B][C][H][W]; w_in: [block_rows][C], rows in the order x_proxy
+    (C_proxy), the raw taps (one slab per enabled direction, TB, BT, LR, RL;
+    within a slab set k and tap t at row k*3 + t), lambda (C_proxy), u
+    (C_proxy); w_out: [C][C_proxy].  Returns z: [B][C][H][W].
+
+    io_round: None for exact fp64 throughout, or a function applied to the
+    four generated tensors and to the scan output, the rounding of a block
+    that stores them in a narrower dtype (round_bf16 for bf16 storage).
+    """
+    x, w_in, w_out = (_f64c(a) for a in (x, w_in, w_out))
+    B, C, H, W = x.shape
+    Cp = w_out.shape[1]
+    nd = bin(dirs & 15).count("1")
+    if w_out.shape != (C, Cp) or cpw < 1 or Cp % cpw:
+        raise ValueError(f"w_out has shape {w_out.shape}; C_proxy must be a multiple of cpw")
+    Cw = Cp // cpw
+    if w_in.shape != (block_rows(Cp, dirs, cpw), C):
+        raise ValueError(f"w_in has shape {w_in.shape}, expected {(block_rows(Cp, dirs, cpw), C)}")
+    rnd = io_round or (lambda a: a)
+    g = np.matmul(w_in, x.reshape(B, C, H * W))            # [B][rows][HW]
+    t0, t1 = Cp, Cp + nd * Cw * 3
+    xp = rnd(g[:, :Cp]).reshape(B, Cp, H, W)
+    taps = rnd(g[:, t0:t1]).reshape(B, nd, Cw, 3, H, W).transpose(1, 0, 2, 3, 4, 5)
+    lam = rnd(g[:, t1:t1 + Cp]).reshape(B, Cp, H, W)
+    u = rnd(g[:, t1 + Cp:]).reshape(B, Cp, H, W)
+    y = rnd(scan_fwd(xp, taps, lam, u, dirs=dirs, groups=groups, cpw=cpw, nthreads=nthreads, lib=lib))
+    return np.matmul(w_out, y.reshape(B, Cp, H * W)).reshape(B, C, H, W)
+
 def slice_fwd(x, w, lam, u, *, dirs: int = 15, groups: int = 1) -> np.ndarray:
     """One slice: x, lam, u [H][W]; w [popcount(dirs)][3][H][W] -> y [H][W]."""
     x, w, lam, u = (_f64c(a) for a in (x, w, lam, u))
