@@ -279,6 +279,86 @@ def cpu_baseline(cfg_name: str, budget_s: float = 8.0, backward: bool = False):
                       f"fp64 C oracle with OpenMP over slices, mean of {reps} runs of {t:.3f} s"}
 
 
+def bench_block(args):
+    """The compressed block on the 1K block workload: tokens per second.
+
+    One step is one gspn_block_fwd call: the input projection (rocBLAS), the
+    scan (libgspn kernels), the output projection (rocBLAS).  The roofline
+    counts the bytes no implementation can avoid (x read, z written, both
+    weight matrices read once) against HBM; the GEMM rate is reported
+    beside it.
+    """
+    import numpy as np
+    import torch
+
+    import linear_spatial_propagation_amd as gspn
+    from linear_spatial_propagation_amd.inputs import BLOCK_CONFIGS, BlockInputs
+
+    cfg = dict(BLOCK_CONFIGS["block1k"])
+    seed = cfg.pop("seed")
+    B, C, Cp, H, W = cfg.pop("B"), cfg.pop("C"), cfg.pop("C_proxy"), cfg.pop("H"), cfg.pop("W")
+    rows = gspn.block_rows(Cp, ch_per_weight=cfg["cpw"])
+    inp = BlockInputs(B, C, Cp, H, W, rows=rows, seed=seed, **cfg)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if inp.dtype == "bf16" else t).to(dev)
+
+    x, wi, wo = up(inp.x_store), up(inp.w_in_store), up(inp.w_out_store)
+    z = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gspn.block_fwd(x, wi, wo, groups=inp.groups, ch_per_weight=inp.cpw, out=z)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(min(args.steps, 50))]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize(dev)
+    per = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+    es = 2 if inp.dtype == "bf16" else 4
+    HW = H * W
+    nbytes = (2 * B * C * HW + rows * C + C * Cp) * es
+    flops = 2 * B * HW * C * (rows + Cp)
+    med = float(np.median(per))
+    out = {
+        "metric": "C-GSPN compressed block forward, tokens/s (projection, scan, projection back)",
+        "value": round(B * HW * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 GEMM inputs, fp32 accumulation; fp32 scan arithmetic",
+        "data": "synthetic",
+        "config": {"workload": f"block1k: B={B} C={C} C_proxy={Cp} H={H} W={W} groups={inp.groups} "
+                               f"ch_per_weight={inp.cpw} dirs=TB|BT|LR|RL, {inp.dtype} I/O",
+                   "w_in_rows": rows, "seed": seed},
+        "launch_us": {"median": round(med * 1e6, 2), "p10": round(float(np.percentile(per, 10)) * 1e6, 2),
+                      "p90": round(float(np.percentile(per, 90)) * 1e6, 2)},
+        "gemm_tflops_at_median": round(flops / med / 1e12, 1),
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / med / 1e9, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(nbytes / med / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "gspn_block_fwd, all launches of one call (x, z and the weights once)"},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,6 +371,8 @@ def main():
                     help="dirs: per-direction lambda and u (gspn_scan_fwd_ex; with --pass bwd, gspn_scan_bwd_ex)")
     ap.add_argument("--batched", type=int, default=1,
                     help="K > 1: K copies of the workload in one batched launch (gspn_scan_fwd_batched)")
+    ap.add_argument("--block", action="store_true",
+                    help="time the compressed block (gspn_block_fwd) on the 1K block workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for counter calibration)")
@@ -313,6 +395,10 @@ def main():
         print(f"bench.py measures one GPU only: the operator has no cross-GPU step, so "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+
+    if args.block:
+        bench_block(args)
+        return
 
     import numpy as np
     import torch

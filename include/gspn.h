@@ -280,6 +280,44 @@ int gspn_scan_bwd_ex(const void *x, const void *w_raw, const void *lam, const vo
                      uint32_t dirs, int32_t groups, int32_t ch_per_weight, uint32_t flags, int32_t dtype,
                      hipStream_t stream);
 
+/*
+ * The compressed propagation block around the scan (GSPN-2 author response,
+ * "Relate Compressive Proxy Dimension to Low-rank Approximation": x is
+ * projected to x_proxy with C_proxy channels by a lightweight linear layer,
+ * the recurrence runs there, and the result is projected back to C; C-GSPN
+ * abstract: a compressed latent-space propagation block).  Per pixel:
+ *   [x_proxy; a; lam; u] = w_in x      (a: the raw taps of the scan)
+ *   y = gspn_scan_fwd(x_proxy, a, lam, u)   over C_proxy channels
+ *   z = w_out y
+ * The pages do not say how the taps, lam and u are generated; here they are
+ * further rows of the input projection (plain linear, no activation).  The
+ * weight normalisation is the scan's own (fused in its kernels).
+ *   x     : [B][C][H][W]
+ *   w_in  : [gspn_block_rows(C_proxy, dirs, ch_per_weight)][C], row-major;
+ *           rows: x_proxy (C_proxy), the raw taps (one slab of
+ *           (C_proxy/ch_per_weight)*3 rows per enabled direction, in bit
+ *           order; set k, tap t at row k*3 + t of its slab), lam (C_proxy),
+ *           u (C_proxy)
+ *   w_out : [C][C_proxy], row-major
+ *   z     : [B][C][H][W], written
+ * The generated tensors and the scan output are stored in `dtype` (bf16:
+ * rounded to nearest even) in a stream-ordered workspace of
+ * (2*rows + C_proxy) * B*H*W elements (rows = gspn_block_rows): the input
+ * projection is one GEMM (x read once) whose row blocks are then copied
+ * into the scan's layouts.  The projections are rocBLAS GEMMs with fp32
+ * accumulation, the scan is gspn_scan_fwd on the automatic path.  Sizes, dirs, groups, ch_per_weight
+ * (which must divide C_proxy) and dtype are checked as in gspn_scan_fwd with
+ * C_proxy in the place of C, and C >= 1; z may not overlap x, w_in or w_out
+ * (GSPN_ERR_ALIAS).  GSPN_ERR_HIP if rocBLAS or a HIP call fails.
+ */
+int gspn_block_fwd(const void *x, const void *w_in, const void *w_out, void *z, int64_t B, int64_t C,
+                   int64_t C_proxy, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
+                   int32_t ch_per_weight, int32_t dtype, hipStream_t stream);
+
+/* Rows of gspn_block_fwd's w_in, 3*C_proxy + 3*popcount(dirs)*(C_proxy/ch_per_weight),
+ * or a negative GSPN_ERR_* code for invalid arguments. */
+int64_t gspn_block_rows(int64_t C_proxy, uint32_t dirs, int32_t ch_per_weight);
+
 /* GSPN_OK if gspn_scan_bwd can run these sizes, GSPN_ERR_PATH if the shape is
  * outside its kernels, or another negative code for invalid sizes. */
 int gspn_bwd_supported(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,

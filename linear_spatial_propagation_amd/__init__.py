@@ -5,6 +5,7 @@
     y = scan_fwd_dirs(x, w_raw, lam_d, u_d, ...)   # per-direction gains / gates
     ys = scan_fwd_batched([dict(x=..., w_raw=..., lam=..., u=...), ...])   # one launch
     y = gspn_scan(x, w_raw, lam, u, ...)   # differentiable: autograd runs scan_bwd
+    z = block_fwd(x, w_in, w_out, ...)     # compressed block: projections around the scan
 
 computes the 4-direction line recurrence of the Generalized Spatial
 Propagation Network with hand-written HIP kernels (libgspn.so, C ABI in
@@ -21,7 +22,8 @@ from . import _lib
 from ._lib import (DIR_ALL, DIR_BT, DIR_LR, DIR_RL, DIR_TB, PATH_AUTO, PATH_FUSED, PATH_GENERAL,
                    GspnError, load, select_path)
 
-__all__ = ["scan_fwd", "scan_bwd", "scan_fwd_dirs", "scan_bwd_dirs", "scan_fwd_batched", "gspn_scan", "select_path", "load", "GspnError", "DIR_TB", "DIR_BT", "DIR_LR", "DIR_RL",
+__all__ = ["scan_fwd", "scan_bwd", "scan_fwd_dirs", "scan_bwd_dirs", "scan_fwd_batched", "gspn_scan", "block_fwd",
+           "block_rows", "select_path", "load", "GspnError", "DIR_TB", "DIR_BT", "DIR_LR", "DIR_RL",
            "DIR_ALL", "PATH_AUTO", "PATH_FUSED", "PATH_GENERAL"]
 
 
@@ -262,5 +264,49 @@ def scan_fwd(x, w_raw, lam, u, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_w
                                out.data_ptr(), B, C, H, W, dirs=dirs, groups=groups,
                                ch_per_weight=ch_per_weight, dtype=_dtype_code(x), path=path,
                                stream=stream)
+    _lib.check(rc)
+    return out
+
+
+def block_rows(C_proxy: int, *, dirs: int = DIR_ALL, ch_per_weight: int = 1) -> int:
+    """Rows of block_fwd's w_in: x_proxy, the raw taps of every enabled
+    direction, lambda and u."""
+    n = _lib.block_rows(C_proxy, dirs, ch_per_weight)
+    _lib.check(n if n < 0 else 0)
+    return n
+
+
+def block_fwd(x, w_in, w_out, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1, out=None):
+    """The compressed propagation block (gspn_block_fwd) on the current stream.
+
+    x: [B, C, H, W]; w_in: [block_rows(C_proxy), C]; w_out: [C, C_proxy];
+    returns z: [B, C, H, W] = w_out (scan of the C_proxy-channel projection
+    of x, with taps, lambda and u projected from x by the further rows of
+    w_in).
+    """
+    import torch
+    for name, t in (("x", x), ("w_in", w_in), ("w_out", w_out)):
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU (HIP) device")
+        if t.device != x.device or t.dtype != x.dtype:
+            raise ValueError(f"{name} must share x's device and dtype")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if x.dim() != 4 or w_in.dim() != 2 or w_out.dim() != 2:
+        raise ValueError("x must be [B, C, H, W], w_in and w_out matrices")
+    B, C, H, W = x.shape
+    Cp = w_out.shape[1]
+    rows = block_rows(Cp, dirs=dirs, ch_per_weight=ch_per_weight)
+    if tuple(w_out.shape) != (C, Cp) or tuple(w_in.shape) != (rows, C):
+        raise ValueError(f"w_in must be [{rows}, {C}] and w_out [{C}, {Cp}]")
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or out.device != x.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        rc = _lib.block_fwd_ptr(x.data_ptr(), w_in.data_ptr(), w_out.data_ptr(), out.data_ptr(), B, C, Cp, H, W,
+                                dirs=dirs, groups=groups, ch_per_weight=ch_per_weight, dtype=_dtype_code(x),
+                                stream=stream)
     _lib.check(rc)
     return out

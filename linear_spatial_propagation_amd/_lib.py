@@ -33,7 +33,8 @@ class Problem(ctypes.Structure):
 
 EXPORTED = ("gspn_scan_fwd", "gspn_scan_fwd_path", "gspn_scan_fwd_ex", "gspn_scan_fwd_batched",
             "gspn_select_path", "gspn_scan_bwd",
-            "gspn_scan_bwd_path", "gspn_scan_bwd_ex", "gspn_bwd_supported", "gspn_status_string", "gspn_last_error", "gspn_version")
+            "gspn_scan_bwd_path", "gspn_scan_bwd_ex", "gspn_bwd_supported", "gspn_block_fwd", "gspn_block_rows",
+            "gspn_status_string", "gspn_last_error", "gspn_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -75,6 +76,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.gspn_scan_bwd_ex.restype = ctypes.c_int
         lib.gspn_bwd_supported.argtypes = [i64, i64, i64, i64, u32, i32, i32, i32]
         lib.gspn_bwd_supported.restype = ctypes.c_int
+        lib.gspn_block_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, u32, i32, i32, i32, vp]
+        lib.gspn_block_fwd.restype = ctypes.c_int
+        lib.gspn_block_rows.argtypes = [i64, u32, i32]
+        lib.gspn_block_rows.restype = ctypes.c_int64
         lib.gspn_status_string.argtypes = [ctypes.c_int]
         lib.gspn_status_string.restype = ctypes.c_char_p
         lib.gspn_last_error.argtypes = []
@@ -142,3 +147,16 @@ def bwd_supported(B, C, H, W, *, dirs=DIR_ALL, groups=1, ch_per_weight=1, dtype=
 
 def select_path(B, C, H, W, *, dirs=DIR_ALL, groups=1, ch_per_weight=1, dtype=GSPN_BF16) -> int:
     return load().gspn_select_path(B, C, H, W, dirs, groups, ch_per_weight, dtype)
+
+
+def block_fwd_ptr(x: int, w_in: int, w_out: int, z: int, B: int, C: int, C_proxy: int, H: int, W: int, *,
+                  dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1, dtype: int = GSPN_BF16,
+                  stream: int = 0) -> int:
+    """Raw call of the compressed block on device pointers; returns the status code."""
+    return load().gspn_block_fwd(x, w_in, w_out, z, B, C, C_proxy, H, W, dirs, groups, ch_per_weight, dtype,
+                                 stream)
+
+
+def block_rows(C_proxy: int, dirs: int = DIR_ALL, ch_per_weight: int = 1) -> int:
+    """Rows of the block's input projection (or a negative status code)."""
+    return load().gspn_block_rows(C_proxy, dirs, ch_per_weight)

@@ -48,7 +48,10 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"hipcc failed on {src}")
         objs.append(obj)
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # rocBLAS runs the block's two projections (plain GEMMs)
+    rocm_lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, f"-L{rocm_lib}",
+           "-lrocblas", f"-Wl,-rpath,{rocm_lib}"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         sys.stderr.write(r.stdout + r.stderr)

@@ -3,6 +3,9 @@
 // The operator and every convention are specified in include/gspn.h.
 #include <hip/hip_runtime.h>
 
+#include <rocblas/rocblas.h>
+
+#include <mutex>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
@@ -299,6 +302,134 @@ int gspn_scan_bwd_ex(const void* x, const void* w_raw, const void* lam, const vo
                      hipStream_t stream) {
     return scan_bwd_impl(x, w_raw, lam, u, gy, gx, gw_raw, glam, gu, B, C, H, W, dirs, groups, ch_per_weight,
                          flags, dtype, GSPN_PATH_AUTO, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- block
+namespace {
+
+std::mutex g_blas_mutex;
+rocblas_handle g_blas[64];   // per device, created on first use
+
+int blas_handle(rocblas_handle* h) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) { set_error("hipGetDevice", e); return GSPN_ERR_HIP; }
+    if (dev < 0 || dev >= 64) { set_error_text("device index out of range"); return GSPN_ERR_HIP; }
+    if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) {
+        g_blas[dev] = nullptr;
+        set_error_text("rocblas_create_handle failed");
+        return GSPN_ERR_HIP;
+    }
+    *h = g_blas[dev];
+    return GSPN_OK;
+}
+
+// For each batch b: Out_b (N x P, row-major, batch stride so) = Wt (N x K,
+// row-major) * In_b (K x P, row-major, batch stride si).  In rocBLAS's
+// column-major terms Out_b^T = In_b^T * Wt^T, with no transposes.
+int gemm_rows(rocblas_handle h, int64_t N, int64_t K, int64_t P, const void* Wt, const void* in, int64_t si,
+              void* out, int64_t so, int64_t batch, bool bf16) {
+    const rocblas_datatype t = bf16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+    const float alpha = 1.0f, beta = 0.0f;
+    const rocblas_status st = rocblas_gemm_strided_batched_ex(
+        h, rocblas_operation_none, rocblas_operation_none, (rocblas_int)P, (rocblas_int)N, (rocblas_int)K, &alpha,
+        in, t, (rocblas_int)P, si, Wt, t, (rocblas_int)K, 0, &beta, out, t, (rocblas_int)P, so, out, t,
+        (rocblas_int)P, so, (rocblas_int)batch, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+    if (st != rocblas_status_success) {
+        snprintf(g_last_error, sizeof(g_last_error), "rocblas_gemm_strided_batched_ex: %s",
+                 rocblas_status_to_string(st));
+        return GSPN_ERR_HIP;
+    }
+    return GSPN_OK;
+}
+
+int64_t block_rows(int64_t Cp, uint32_t dirs, int32_t cpw) {
+    return 3 * Cp + 3 * (int64_t)popcount4(dirs) * (Cp / cpw);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t gspn_block_rows(int64_t C_proxy, uint32_t dirs, int32_t ch_per_weight) {
+    if (C_proxy <= 0) return GSPN_ERR_SHAPE;
+    if (dirs == 0 || (dirs & ~15u)) return GSPN_ERR_DIRS;
+    if (ch_per_weight < 1 || C_proxy % ch_per_weight) return GSPN_ERR_CPW;
+    return block_rows(C_proxy, dirs, ch_per_weight);
+}
+
+int gspn_block_fwd(const void* x, const void* w_in, const void* w_out, void* z, int64_t B, int64_t C,
+                   int64_t C_proxy, int64_t H, int64_t W, uint32_t dirs, int32_t groups, int32_t ch_per_weight,
+                   int32_t dtype, hipStream_t stream) {
+    g_last_error[0] = '\0';
+    if (C <= 0 || C > (1LL << 22)) return GSPN_ERR_SHAPE;
+    int rc = check_sizes(B, C_proxy, H, W, dirs, groups, ch_per_weight, dtype);
+    if (rc) return rc;
+    if (B * C > (1LL << 22)) return GSPN_ERR_SHAPE;
+    if (!x || !w_in || !w_out || !z) return GSPN_ERR_NULL;
+    const void* ptrs[4] = {x, w_in, w_out, z};
+    for (const void* q : ptrs)
+        if ((uintptr_t)q & 15u) return GSPN_ERR_ALIGN;
+    const bool bf16 = dtype == GSPN_BF16;
+    const size_t es = bf16 ? 2 : 4;
+    const int64_t HW = H * W, Cp = C_proxy, Cw = C_proxy / ch_per_weight;
+    const int64_t nd = popcount4(dirs), rows = block_rows(Cp, dirs, ch_per_weight);
+    const size_t xbytes = (size_t)B * C * HW * es;
+    if (overlaps(z, xbytes, x, xbytes) || overlaps(z, xbytes, w_in, (size_t)rows * C * es) ||
+        overlaps(z, xbytes, w_out, (size_t)C * Cp * es))
+        return GSPN_ERR_ALIAS;
+    // the GEMM sizes are 32-bit in rocBLAS
+    if (HW > INT32_MAX || rows > INT32_MAX || C > INT32_MAX) return GSPN_ERR_SHAPE;
+
+    // workspace: g (the input projection, [B][rows][HW]) | x_proxy | taps
+    // (nd slabs) | lam | u | y, each 256-byte aligned
+    auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const size_t ep = (size_t)B * Cp * HW * es, et = (size_t)nd * B * Cw * 3 * HW * es;
+    const size_t o_g = 0, o_x = al((size_t)B * rows * HW * es), o_t = o_x + al(ep), o_l = o_t + al(et),
+                 o_u = o_l + al(ep), o_y = o_u + al(ep);
+    const size_t total = o_y + al(ep);
+    char* work = nullptr;
+    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&work), total, stream);
+    if (e != hipSuccess) { set_error("hipMallocAsync(workspace)", e); return GSPN_ERR_HIP; }
+
+    rc = GSPN_OK;
+    {
+        std::lock_guard<std::mutex> lock(g_blas_mutex);
+        rocblas_handle h = nullptr;
+        rc = blas_handle(&h);
+        if (rc == GSPN_OK && rocblas_set_stream(h, stream) != rocblas_status_success) {
+            set_error_text("rocblas_set_stream failed");
+            rc = GSPN_ERR_HIP;
+        }
+        // one GEMM reads x once: g_b = w_in x_b, [B][rows][HW]
+        if (rc == GSPN_OK) rc = gemm_rows(h, rows, C, HW, w_in, x, C * HW, work + o_g, rows * HW, B, bf16);
+        // its row blocks into the scan's layouts: x_proxy, lam, u [B][C_proxy][HW],
+        // the taps of slab s into [nd][B][Cw*3][HW] (strided 2D copies)
+        const size_t pitch = (size_t)rows * HW * es;
+        auto rows_to = [&](char* dst, int64_t r0, int64_t nr, size_t dst_pitch) {
+            if (rc != GSPN_OK) return;
+            const hipError_t ec = hipMemcpy2DAsync(dst, dst_pitch, work + o_g + (size_t)r0 * HW * es, pitch,
+                                                   (size_t)nr * HW * es, (size_t)B, hipMemcpyDeviceToDevice, stream);
+            if (ec != hipSuccess) { set_error("hipMemcpy2DAsync", ec); rc = GSPN_ERR_HIP; }
+        };
+        rows_to(work + o_x, 0, Cp, (size_t)Cp * HW * es);
+        for (int64_t sl = 0; sl < nd; ++sl)
+            rows_to(work + o_t + (size_t)sl * B * Cw * 3 * HW * es, Cp + sl * Cw * 3, Cw * 3,
+                    (size_t)Cw * 3 * HW * es);
+        rows_to(work + o_l, Cp + nd * Cw * 3, Cp, (size_t)Cp * HW * es);
+        rows_to(work + o_u, 2 * Cp + nd * Cw * 3, Cp, (size_t)Cp * HW * es);
+        if (rc == GSPN_OK)
+            rc = scan_fwd_impl(work + o_x, work + o_t, work + o_l, work + o_u, work + o_y, B, Cp, H, W, dirs,
+                               groups, ch_per_weight, 0u, dtype, GSPN_PATH_AUTO, stream);
+        // z: [B][C][HW] = w_out (C x C_proxy) * y_b
+        if (rc == GSPN_OK) rc = gemm_rows(h, C, Cp, HW, w_out, work + o_y, Cp * HW, z, C * HW, B, bf16);
+    }
+    const hipError_t ef = hipFreeAsync(work, stream);
+    if (rc != GSPN_OK) return rc;
+    if (ef != hipSuccess) { set_error("hipFreeAsync(workspace)", ef); return GSPN_ERR_HIP; }
+    return GSPN_OK;
 }
 
 }  // extern "C"

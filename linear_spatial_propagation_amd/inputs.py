@@ -194,3 +194,34 @@ CONFIGS = {
 def config_workload(name: str, dirs: int = 15) -> Workload:
     cfg = dict(CONFIGS[name])
     return make_workload(cfg.pop("B"), cfg.pop("C"), cfg.pop("H"), cfg.pop("W"), dirs=dirs, **cfg)
+
+
+# The 1K C-GSPN block: batch 32, C = 1152 (C-GSPN abstract), projected to a
+# 128-channel proxy that the scan runs on (the cgspn1k scan workload).
+BLOCK_CONFIGS = {
+    "block1k": dict(B=32, C=1152, C_proxy=128, H=64, W=64, groups=1, cpw=8, dtype="bf16", seed=5),
+}
+
+
+class BlockInputs:
+    """Seeded inputs of the compressed block in the storage dtype (bf16 bit
+    patterns or fp32) and their exact fp64 values.
+
+    x ~ N(0, 1); w_in ~ N(0, 1/C), so that the projected x_proxy, taps,
+    lambda and u are of unit scale; w_out ~ N(0, 1/C_proxy).
+    """
+
+    def __init__(self, B, C, C_proxy, H, W, *, rows, dirs=15, groups=1, cpw=1, dtype="bf16", seed=0):
+        self.B, self.C, self.C_proxy, self.H, self.W = B, C, C_proxy, H, W
+        self.dirs, self.groups, self.cpw, self.dtype, self.rows = dirs, groups, cpw, dtype, rows
+        rng = np.random.default_rng(seed)
+        self.x_store = _store(rng.standard_normal((B, C, H, W), dtype=np.float32), dtype)
+        self.w_in_store = _store(rng.standard_normal((rows, C), dtype=np.float32) / np.float32(np.sqrt(C)), dtype)
+        self.w_out_store = _store(rng.standard_normal((C, C_proxy), dtype=np.float32) /
+                                  np.float32(np.sqrt(C_proxy)), dtype)
+
+    def _f64(self, a):
+        return bf16_bits_to_f32(a).astype(np.float64) if self.dtype == "bf16" else a.astype(np.float64)
+
+    def f64(self):
+        return self._f64(self.x_store), self._f64(self.w_in_store), self._f64(self.w_out_store)

@@ -221,3 +221,33 @@ def test_variant_bwd_invalid_arguments_rejected_on_host(lib, kw, code):
 def test_variant_bwd_flags_zero_is_the_shared_backward(lib):
     assert call_bwd_ex(flags=0, H=130) == call_bwd(H=130) == -10
     assert call_bwd_ex(flags=0, gx=FAKE) == -8
+
+
+def call_block(**kw):
+    args = dict(x=FAKE, w_in=FAKE + (1 << 32), w_out=FAKE + (2 << 32), z=FAKE + (3 << 32), B=2, C=24, C_proxy=8,
+                H=16, W=16, dirs=15, groups=1, ch_per_weight=2, dtype=1)
+    args.update(kw)
+    return _lib.block_fwd_ptr(args["x"], args["w_in"], args["w_out"], args["z"], args["B"], args["C"],
+                              args["C_proxy"], args["H"], args["W"], dirs=args["dirs"], groups=args["groups"],
+                              ch_per_weight=args["ch_per_weight"], dtype=args["dtype"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(C=0), -2), (dict(C_proxy=0), -2), (dict(W=4097), -2), (dict(B=1 << 20, C=1 << 10), -2),
+    (dict(dirs=0), -3), (dict(dirs=16), -3), (dict(groups=3), -4), (dict(ch_per_weight=3), -5),
+    (dict(dtype=2), -6), (dict(x=0), -1), (dict(w_in=0), -1), (dict(w_out=0), -1), (dict(z=0), -1),
+    (dict(z=FAKE + (3 << 32) + 8), -7),
+    (dict(z=FAKE), -8),                              # z on x
+    (dict(z=FAKE + (1 << 32) + 1024), -8),           # z inside w_in
+    (dict(z=FAKE + (2 << 32) - 256), -8),            # z runs into w_out
+])
+def test_block_invalid_arguments_rejected_on_host(lib, kw, code):
+    assert call_block(**kw) == code
+
+
+def test_block_rows(lib):
+    assert _lib.block_rows(128, 15, 8) == 3 * 128 + 3 * 4 * 16
+    assert _lib.block_rows(8, 5, 2) == 24 + 3 * 2 * 4
+    assert _lib.block_rows(0, 15, 1) == -2
+    assert _lib.block_rows(8, 0, 1) == -3
+    assert _lib.block_rows(8, 15, 3) == -5
