@@ -383,13 +383,15 @@ int gspn_block_fwd(const void* x, const void* w_in, const void* w_out, void* z, 
     // the GEMM sizes are 32-bit in rocBLAS
     if (HW > INT32_MAX || rows > INT32_MAX || C > INT32_MAX) return GSPN_ERR_SHAPE;
 
-    // workspace: g (the input projection, [B][rows][HW]) | x_proxy | taps
-    // (nd slabs) | lam | u | y, each 256-byte aligned
+    // workspace: g (the input projection, [B][rows][HW]) | y | and, unless
+    // the fused scan reads g in place, x_proxy | taps (nd slabs) | lam | u;
+    // each 256-byte aligned
+    const bool in_place = auto_path(H, W) == GSPN_PATH_FUSED;
     auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
     const size_t ep = (size_t)B * Cp * HW * es, et = (size_t)nd * B * Cw * 3 * HW * es;
-    const size_t o_g = 0, o_x = al((size_t)B * rows * HW * es), o_t = o_x + al(ep), o_l = o_t + al(et),
-                 o_u = o_l + al(ep), o_y = o_u + al(ep);
-    const size_t total = o_y + al(ep);
+    const size_t o_g = 0, o_y = al((size_t)B * rows * HW * es), o_x = o_y + al(ep), o_t = o_x + al(ep),
+                 o_l = o_t + al(et), o_u = o_l + al(ep);
+    const size_t total = in_place ? o_x : o_u + al(ep);
     char* work = nullptr;
     hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&work), total, stream);
     if (e != hipSuccess) { set_error("hipMallocAsync(workspace)", e); return GSPN_ERR_HIP; }
@@ -405,8 +407,26 @@ int gspn_block_fwd(const void* x, const void* w_in, const void* w_out, void* z, 
         }
         // one GEMM reads x once: g_b = w_in x_b, [B][rows][HW]
         if (rc == GSPN_OK) rc = gemm_rows(h, rows, C, HW, w_in, x, C * HW, work + o_g, rows * HW, B, bf16);
-        // its row blocks into the scan's layouts: x_proxy, lam, u [B][C_proxy][HW],
-        // the taps of slab s into [nd][B][Cw*3][HW] (strided 2D copies)
+        // The fused scan reads g in place: x_proxy, lam and u are row blocks of
+        // g with a batch stride of `rows` planes, and the taps of slab s start
+        // at row C_proxy + s*Cw*3.  The other paths take contiguous tensors:
+        // g's row blocks are copied into x_proxy, lam, u [B][C_proxy][HW] and
+        // the taps [nd][B][Cw*3][HW] (strided 2D copies).
+        if (in_place && rc == GSPN_OK) {
+            gspn::ScanArgs a;
+            const size_t plane = (size_t)HW * es;
+            a.x = work + o_g;
+            a.w = work + o_g + (size_t)Cp * plane;
+            a.lam = work + o_g + (size_t)(Cp + nd * Cw * 3) * plane;
+            a.u = work + o_g + (size_t)(2 * Cp + nd * Cw * 3) * plane;
+            a.y = work + o_y;
+            a.B = (int)B; a.C = (int)Cp; a.H = (int)H; a.W = (int)W;
+            a.dirs = dirs; a.groups = groups; a.cpw = ch_per_weight; a.bf16 = bf16;
+            a.lam_dir = a.u_dir = 0;
+            a.x_bplanes = (int)rows; a.w_bplanes = (int)rows; a.w_splanes = (int)(Cw * 3);
+            const hipError_t el = gspn::launch_fused(a, stream);
+            if (el != hipSuccess) { set_error("fused kernel launch", el); rc = GSPN_ERR_HIP; }
+        }
         const size_t pitch = (size_t)rows * HW * es;
         auto rows_to = [&](char* dst, int64_t r0, int64_t nr, size_t dst_pitch) {
             if (rc != GSPN_OK) return;
@@ -414,13 +434,15 @@ int gspn_block_fwd(const void* x, const void* w_in, const void* w_out, void* z, 
                                                    (size_t)nr * HW * es, (size_t)B, hipMemcpyDeviceToDevice, stream);
             if (ec != hipSuccess) { set_error("hipMemcpy2DAsync", ec); rc = GSPN_ERR_HIP; }
         };
-        rows_to(work + o_x, 0, Cp, (size_t)Cp * HW * es);
-        for (int64_t sl = 0; sl < nd; ++sl)
-            rows_to(work + o_t + (size_t)sl * B * Cw * 3 * HW * es, Cp + sl * Cw * 3, Cw * 3,
-                    (size_t)Cw * 3 * HW * es);
-        rows_to(work + o_l, Cp + nd * Cw * 3, Cp, (size_t)Cp * HW * es);
-        rows_to(work + o_u, 2 * Cp + nd * Cw * 3, Cp, (size_t)Cp * HW * es);
-        if (rc == GSPN_OK)
+        if (!in_place) {
+            rows_to(work + o_x, 0, Cp, (size_t)Cp * HW * es);
+            for (int64_t sl = 0; sl < nd; ++sl)
+                rows_to(work + o_t + (size_t)sl * B * Cw * 3 * HW * es, Cp + sl * Cw * 3, Cw * 3,
+                        (size_t)Cw * 3 * HW * es);
+            rows_to(work + o_l, Cp + nd * Cw * 3, Cp, (size_t)Cp * HW * es);
+            rows_to(work + o_u, 2 * Cp + nd * Cw * 3, Cp, (size_t)Cp * HW * es);
+        }
+        if (rc == GSPN_OK && !in_place)
             rc = scan_fwd_impl(work + o_x, work + o_t, work + o_l, work + o_u, work + o_y, B, Cp, H, W, dirs,
                                groups, ch_per_weight, 0u, dtype, GSPN_PATH_AUTO, stream);
         // z: [B][C][HW] = w_out (C x C_proxy) * y_b

@@ -58,6 +58,9 @@ struct FusedParams {
     uint32_t dirs;
     int nchunk;     // channel chunks per weight set
     int chunk_len;  // channels per chunk
+    // layout strides in H*W planes: x / lam / u between batch items; w
+    // between batch items and between direction slabs
+    int x_bplanes, w_bplanes, w_splanes;
 };
 
 // 16-byte access = N elements.
@@ -318,10 +321,10 @@ template <typename T>
 struct TapSrc {
     const T* w;
     uint32_t dirs;
-    int B, b, Cw, k, HW;
+    int splanes, bplanes, b, k, HW;   // planes between direction slabs / batch items
     __device__ __forceinline__ const T* dir(int dd) const {
         const int slab = __builtin_popcount(dirs & ((1u << dd) - 1u));
-        return w + ((size_t)(slab * B + b) * Cw + k) * 3 * (size_t)HW;
+        return w + ((size_t)slab * splanes + (size_t)b * bplanes + (size_t)k * 3) * (size_t)HW;
     }
 };
 
@@ -453,7 +456,7 @@ __device__ __forceinline__ void fused_scan_body(const FusedParams& prm, const in
     const T* __restrict__ gu = static_cast<const T*>(prm.u);
     T* __restrict__ gy = static_cast<T*>(prm.y);
 
-    const int H = prm.H, W = prm.W, B = prm.B, C = prm.C, Cw = prm.Cw;
+    const int H = prm.H, W = prm.W, C = prm.C, Cw = prm.Cw;
     const int HW = H * W;
     const uint32_t dirs = prm.dirs;
     constexpr bool vec = VEC;
@@ -493,7 +496,7 @@ __device__ __forceinline__ void fused_scan_body(const FusedParams& prm, const in
     const bool row_any = (dirs & 3u) != 0;
     const bool col_any = (dirs & 12u) != 0;
     auto load_rows = [&](const T* __restrict__ g, int c, uint4 (&dst)[kMaxIt]) {
-        const T* __restrict__ sl = g + ((size_t)b * C + c) * (size_t)HW;
+        const T* __restrict__ sl = g + ((size_t)b * prm.x_bplanes + c) * (size_t)HW;
 #pragma unroll
         for (int it = 0; it < kMaxIt; ++it) {
             const int r = tr + it * rpi;
@@ -550,7 +553,7 @@ __device__ __forceinline__ void fused_scan_body(const FusedParams& prm, const in
     const int first_line = asc ? 0 : n - 1;
     {
         float* S = lds;   // [4][3][kChunk][kPitch]
-        const TapSrc<T> wsrc{gw, dirs, B, b, Cw, k, HW};
+        const TapSrc<T> wsrc{gw, dirs, prm.w_splanes, prm.w_bplanes, b, k, HW};
         constexpr int kNCh = kS / kChunk;
         constexpr int kLd = TapChunk<T>::kLoads;
 #ifndef GSPN_TAP_AHEAD
@@ -595,7 +598,7 @@ __device__ __forceinline__ void fused_scan_body(const FusedParams& prm, const in
                         constexpr int q = g - kTapItems;
                         constexpr int it = q % kMaxIt;
                         const int r = min(tr + it * rpi, H - 1);
-                        const size_t o = ((size_t)b * C + c_begin) * (size_t)HW + r * W + col0;
+                        const size_t o = ((size_t)b * prm.x_bplanes + c_begin) * (size_t)HW + r * W + col0;
                         if constexpr (q / kMaxIt == 0) x1[it] = load16(gx + o);
                         else if constexpr (q / kMaxIt == 1) l1[it] = load16(glam + o);
                         else u0[it] = load16(gu + o);
@@ -757,6 +760,9 @@ FusedParams fused_params(const ScanArgs& a) {
     p.x = a.x; p.w = a.w; p.lam = a.lam; p.u = a.u; p.y = a.y;
     p.B = a.B; p.C = a.C; p.H = a.H; p.W = a.W;
     p.cpw = a.cpw; p.Cw = a.C / a.cpw; p.groups = a.groups; p.dirs = a.dirs;
+    p.x_bplanes = a.x_bplanes ? a.x_bplanes : a.C;
+    p.w_bplanes = a.w_bplanes ? a.w_bplanes : p.Cw * 3;
+    p.w_splanes = a.w_splanes ? a.w_splanes : a.B * p.Cw * 3;
     return p;
 }
 

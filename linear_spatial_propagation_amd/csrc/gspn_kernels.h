@@ -20,6 +20,11 @@ struct ScanArgs {
     int bf16;     // 1: bf16 storage, 0: fp32 storage
     int lam_dir;  // 1: lam holds one [B][C][H][W] slab per enabled direction (line path only)
     int u_dir;    // 1: u holds one slab per enabled direction, y = sum_d u_d h_d (line path only)
+    // Fused path only: strides in H*W planes, 0 for the contiguous layout.
+    // x, lam and u: planes between batch items (default C); w: planes
+    // between batch items (default (C/cpw)*3) and between direction slabs
+    // (default B*(C/cpw)*3).  y is always contiguous.
+    int x_bplanes = 0, w_bplanes = 0, w_splanes = 0;
 };
 
 // Fused 4-direction kernel: H <= 64 and W <= 64.
