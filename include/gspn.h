@@ -301,11 +301,13 @@ int gspn_scan_bwd_ex(const void *x, const void *w_raw, const void *lam, const vo
  *   w_out : [C][C_proxy], row-major
  *   z     : [B][C][H][W], written
  * The generated tensors and the scan output are stored in `dtype` (bf16:
- * rounded to nearest even) in a stream-ordered workspace of
- * (2*rows + C_proxy) * B*H*W elements (rows = gspn_block_rows): the input
- * projection is one GEMM (x read once) whose row blocks are then copied
- * into the scan's layouts.  The projections are rocBLAS GEMMs with fp32
- * accumulation, the scan is gspn_scan_fwd on the automatic path.  Sizes, dirs, groups, ch_per_weight
+ * rounded to nearest even) in a stream-ordered workspace.  The input
+ * projection is one GEMM (x read once) into g = [B][rows][H*W] (rows =
+ * gspn_block_rows).  For H, W <= 64 the fused scan reads g in place
+ * (workspace (rows + C_proxy) * B*H*W elements); otherwise g's row blocks
+ * are copied into contiguous tensors and the scan is gspn_scan_fwd on the
+ * automatic path (workspace (2*rows + C_proxy) * B*H*W elements).  The
+ * projections are rocBLAS GEMMs with fp32 accumulation.  Sizes, dirs, groups, ch_per_weight
  * (which must divide C_proxy) and dtype are checked as in gspn_scan_fwd with
  * C_proxy in the place of C, and C >= 1; z may not overlap x, w_in or w_out
  * (GSPN_ERR_ALIAS).  GSPN_ERR_HIP if rocBLAS or a HIP call fails.
