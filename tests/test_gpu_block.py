@@ -66,6 +66,9 @@ CASES = [
     (2, 16, 4, 72, 40, 15, 2, 1),     # line kernels, local groups
     (1, 20, 6, 9, 7, 5, 1, 3),        # TB and LR, ragged sides
     (3, 8, 16, 12, 12, 15, 4, 4),     # proxy wider than the input
+    (2, 64, 32, 16, 16, 15, 1, 4),
+    (1, 96, 64, 24, 40, 15, 1, 8),
+    (2, 160, 128, 8, 16, 15, 2, 16),  # the proxy width of the 1K block
 ]
 
 
