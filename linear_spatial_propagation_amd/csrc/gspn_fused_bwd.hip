@@ -28,8 +28,14 @@
 //    D_t - sum_v w_v D_v is a cancellation-free expression in E0, E2 and
 //    the weights.
 //  * The prologue also keeps, per pixel, the sum S of the sigmoids of its
-//    existing taps, so that the epilogue gets 1 - sigmoid(a_t) = 1 - w_t S
-//    without exponentials and writes the tap gradients of the set once.
+//    existing taps, so that the epilogue gets sigmoid(a_t) = w_t S.  It forms
+//    1 - sigmoid(a_t) as 1 - w_t S below 1/2 and as exp(-a_t) w_t S above (no
+//    cancellation), reading the raw taps again, and writes the tap gradients
+//    of the set once.
+//  * The prologue and the epilogue take 16 slots at a time.  Column
+//    directions read and write a lane's own row as 16-byte vectors; row
+//    directions hold the chunk transposed (lane = slot and 16 positions) so
+//    that they read and write 16-byte row vectors too.
 #include "gspn_lines.h"
 
 namespace gspn {
