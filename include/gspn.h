@@ -307,7 +307,10 @@ int gspn_scan_bwd_ex(const void *x, const void *w_raw, const void *lam, const vo
  * (workspace (rows + C_proxy) * B*H*W elements); otherwise g's row blocks
  * are copied into contiguous tensors and the scan is gspn_scan_fwd on the
  * automatic path (workspace (2*rows + C_proxy) * B*H*W elements).  The
- * projections are rocBLAS GEMMs with fp32 accumulation.  Sizes, dirs, groups, ch_per_weight
+ * projections are rocBLAS GEMMs with fp32 accumulation.  The first call on a
+ * device creates a rocBLAS handle that the library keeps until the process
+ * ends (the scan entry points hold no state); calls are serialised on it by
+ * a mutex while they enqueue, and only enqueue work on `stream`.  Sizes, dirs, groups, ch_per_weight
  * (which must divide C_proxy) and dtype are checked as in gspn_scan_fwd with
  * C_proxy in the place of C, and C >= 1; z may not overlap x, w_in or w_out
  * (GSPN_ERR_ALIAS).  GSPN_ERR_HIP if rocBLAS or a HIP call fails.
