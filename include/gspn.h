@@ -210,8 +210,8 @@ int gspn_select_path(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, 
  * Backward of gspn_scan_fwd: the exact vector-Jacobian product of the
  * definition above for a loss L with dL/dy = gy.  The pages give no formulas
  * for it ("GSPN-2: Efficient Parallel Sequence Modeling", author response,
- * "How Channel-shared Weight Mitigates the Concurrency Bottleneck?", states
- * only that the backward gains as much as the forward); with
+ * "Backward Benchmark", states only that the backward's launch design and
+ * speed-up follow the forward's); with
  * S = sum over enabled d of h_d and g_d the adjoint state of direction d:
  *   gu   = gy * S
  *   g_d  : for the lines of each group from its last line back to its first,

@@ -4,8 +4,7 @@
 // operator ("Parallel Sequence Modeling via Generalized Spatial Propagation
 // Network", CVPR 2025 paper notes, "Key design 1-3"; the GSPN-2 author
 // response notes that the backward runs with the same speed-up as the
-// forward, "How Channel-shared Weight Mitigates the Concurrency
-// Bottleneck?").  With S = sum_dir h_dir and G = sum_dir g_dir:
+// forward, "Backward Benchmark").  With S = sum_dir h_dir and G = sum_dir g_dir:
 //   gu = gy * S;   gx = lam * G;   glam = x * G
 //   g_i = gy*u (at line i) + w_{i+1}^T g_{i+1}   (adjoint, last line first;
 //         the second term is cut at the first line of a group)

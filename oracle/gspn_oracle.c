@@ -244,8 +244,9 @@ int gspn_oracle_max_threads(void)
 /* ------------------------------------------------------------------------
  * Backward: the exact vector-Jacobian product of the forward above.
  *
- * The pages state only that a backward pass exists and runs about as fast
- * as the forward ("GSPN-2" notes, implementation section); the gradients
+ * The pages state only that a backward pass exists and gains about as much
+ * as the forward ("GSPN-2: Efficient Parallel Sequence Modeling", author
+ * response, paragraph "Backward Benchmark"); the gradients
  * below are the chain rule applied to the forward's definition, written out
  * step by step:
  *

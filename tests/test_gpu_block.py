@@ -3,41 +3,30 @@
 The block is z = w_out . scan(x_proxy, taps, lambda, u) with x_proxy, taps,
 lambda and u projected from x by w_in (oracle.block_fwd states the reading).
 
-Metric: for every output element i, with the oracle value zhat_i,
-    err = max_i |z_i - zhat_i| / s_i,   s_i = (|w_out| |y|)_i
-the sum of the magnitudes of the terms the output projection adds (floored
-at 0.1 of its rms), so that outputs that cancel are not divided by ~0.
+Metric (tests/parity.py, block_error): r_i = |z_i - zhat_i|, less the half
+ulp of z_i's own bf16 rounding for bf16 I/O;
+    pointwise = max_i r_i / s_i,   s_i = (|w_out| |y|)_i
+(the sum of the magnitudes of the terms the output projection adds, floored
+at 0.1 of its rms), and l2 = ||r|| / ||zhat||.
 
-- fp32 I/O: the oracle is exact.  The GEMMs accumulate in fp32 (relative
-  error about K 2^-24 with K <= 1152, below 1e-4) and the scan meets its own
-  1e-4 bound, so err <= 2e-4.
-- bf16 I/O: the block stores x_proxy, taps, lambda, u and y in bf16, and the
-  oracle rounds the same tensors (oracle.round_bf16).  What remains is the
-  final rounding of z (half an ulp, 2^-9 relative), the scan's own 2e-3
-  bound, and the rare intermediate whose fp32 GEMM sum and fp64 sum round to
-  neighbouring bf16 values (one ulp, 2^-8 relative, at that element only):
-  err <= 1e-2.
+- fp32 I/O: the oracle is exact; the GEMMs accumulate in fp32 (about
+  K 2^-24 relative with K <= 1152) and the scan meets its own 1e-4, so
+  pointwise <= 2e-4 and l2 <= 2e-5.
+- bf16 I/O: the block stores x_proxy, taps, lambda, u and y in bf16 and the
+  oracle rounds the same tensors (oracle.round_bf16).  pointwise <= 2e-3
+  (the scan's bf16 bound) and l2 <= 3e-4: a correct block differs only where
+  an intermediate's fp32 and fp64 values round to neighbouring bf16 numbers,
+  while a truncating or misplaced rounding moves every intermediate and puts
+  l2 above 1e-3 (tests/test_block_metric.py plants those mistakes).
 """
 import numpy as np
 import pytest
 
 import oracle
-from parity import from_device, say, to_device
+from parity import BLOCK_TOL, block_error, block_passes, from_device, say, to_device
 from linear_spatial_propagation_amd.inputs import BLOCK_CONFIGS, BlockInputs
 
 pytestmark = pytest.mark.gpu
-
-TOL = {"f32": 2e-4, "bf16": 1e-2}
-
-
-def block_error(z, zhat, w_out, y_abs):
-    s = np.einsum("cq,bqhw->bchw", np.abs(w_out), y_abs)
-    rms = float(np.sqrt(np.mean(s * s)))
-    s = np.maximum(s, 0.1 * rms)
-    if not np.all(np.isfinite(z)):
-        return float("inf")
-    return float((np.abs(z - zhat) / s).max())
-
 
 def run_block(inp, out_batches=None):
     import torch
@@ -84,9 +73,9 @@ def test_block_parity(case, dtype):
     rnd = oracle.round_bf16 if dtype == "bf16" else None
     x, wi, _ = inp.f64()
     y = _scan_out(inp, x, wi, rnd)
-    err = block_error(z, zhat, wo, np.abs(y))
-    say(f"  err {err:.3e} (tol {TOL[dtype]:.0e})")
-    assert err <= TOL[dtype]
+    err = block_error(z, zhat, wo, np.abs(y), dtype)
+    say(f"  pointwise {err['pointwise']:.3e} l2 {err['l2']:.3e} (tol {BLOCK_TOL[dtype]})")
+    assert block_passes(err, dtype), err
 
 
 def _scan_out(inp, x, wi, rnd):
@@ -114,9 +103,9 @@ def test_block1k_sampled_batches():
     zhat, wo = oracle_block(inp, batches=sel)
     x, wi, _ = inp.f64()
     y = _scan_out(inp, x[sel], wi, oracle.round_bf16)
-    err = block_error(z, zhat, wo, np.abs(y))
-    say(f"  err {err:.3e} (tol {TOL['bf16']:.0e})")
-    assert err <= TOL["bf16"]
+    err = block_error(z, zhat, wo, np.abs(y), "bf16")
+    say(f"  pointwise {err['pointwise']:.3e} l2 {err['l2']:.3e} (tol {BLOCK_TOL['bf16']})")
+    assert block_passes(err, "bf16"), err
 
 
 def test_block_rejects_bad_weights():

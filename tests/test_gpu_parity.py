@@ -143,10 +143,18 @@ def test_edge_shapes_general(case, dtype):
           path="general")
 
 
-def test_fused_and_general_paths_agree_bitwise_where_rounding_allows():
+def test_fused_and_line_paths_agree_to_fp32_rounding():
+    # the fused kernel and the line kernels sum in different orders, so their
+    # fp32 results may differ in the last bits; each meets the oracle bound,
+    # and they agree with each other within a few fp32 roundings of the
+    # accumulated state (64 lines, about 64 * 2^-24 relative)
     wl = make_workload(2, 8, 40, 40, cpw=2, dtype="f32", seed=5)
     y1 = run_workload(wl, PATHS["fused"])
     y2 = run_workload(wl, PATHS["general"])
     yhat = oracle.scan_fwd(wl.x, wl.w, wl.lam, wl.u, cpw=2)
     assert parity_error(y1, yhat, "f32") <= 1e-4
     assert parity_error(y2, yhat, "f32") <= 1e-4
+    scale = np.maximum(np.abs(yhat), 0.1 * np.sqrt(np.mean(yhat ** 2)))
+    between = float((np.abs(y1 - y2) / scale).max())
+    say(f"  fused vs line kernels: {between:.3e}")
+    assert between <= 64 * 2.0 ** -24 * 4

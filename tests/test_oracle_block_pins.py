@@ -21,7 +21,11 @@ import oracle
 from bruteforce import bruteforce_fwd
 
 
-def _block_loops(x, w_in, w_out, dirs, groups, cpw):
+def _block_loops(x, w_in, w_out, dirs, groups, cpw, rnd=None):
+    """The block by pixel loops; rnd (if given) rounds each generated value
+    and each scan output one at a time, the places a block that stores its
+    intermediates in a narrower dtype rounds them."""
+    rnd = rnd or (lambda v: v)
     B, C, H, W = x.shape
     Cp = w_out.shape[1]
     nd = bin(dirs).count("1")
@@ -35,7 +39,7 @@ def _block_loops(x, w_in, w_out, dirs, groups, cpw):
                     s = 0.0
                     for c in range(C):
                         s += w_in[r, c] * x[b, c, i, j]
-                    g[b, r, i, j] = s
+                    g[b, r, i, j] = rnd(s)
     xp = g[:, :Cp]
     taps = np.zeros((nd, B, Cw, 3, H, W))
     for sl in range(nd):
@@ -46,6 +50,7 @@ def _block_loops(x, w_in, w_out, dirs, groups, cpw):
     lam = g[:, base:base + Cp]
     u = g[:, base + Cp:base + 2 * Cp]
     y = bruteforce_fwd(xp, taps, lam, u, dirs=dirs, groups=groups, cpw=cpw)
+    y = np.vectorize(rnd)(y)
     z = np.zeros((B, C, H, W))
     for b in range(B):
         for c in range(C):
@@ -132,3 +137,33 @@ def test_round_bf16_ties_and_torch():
     r32 = r.astype(np.float32).astype(np.float64)
     np.testing.assert_array_equal(oracle.round_bf16(r32),
                                   torch.tensor(r32, dtype=torch.float32).to(torch.bfloat16).double().numpy())
+
+
+def _bf16_scalar(v):
+    """One value rounded to bfloat16 by torch's own conversion (through
+    float32, round to nearest even), as fp64."""
+    torch = pytest.importorskip("torch")
+    return float(torch.tensor(float(v), dtype=torch.float32).to(torch.bfloat16).double())
+
+
+@pytest.mark.parametrize("case", [
+    (1, 3, 2, 3, 4, 15, 1, 1),
+    (2, 4, 4, 4, 4, 6, 2, 2),
+])
+def test_block_io_rounding_placement(case):
+    # io_round rounds exactly the five stored tensors: x_proxy, the taps,
+    # lambda and u as the input projection produces them, and the scan output
+    # before the output projection (z itself is left to the caller's dtype)
+    B, C, Cp, H, W, dirs, groups, cpw = case
+    rng = np.random.default_rng(100 + sum(case))
+    x = rng.standard_normal((B, C, H, W))
+    w_in = rng.standard_normal((oracle.block_rows(Cp, dirs, cpw), C)) * 0.7
+    w_out = rng.standard_normal((C, Cp))
+    z = oracle.block_fwd(x, w_in, w_out, dirs=dirs, groups=groups, cpw=cpw, io_round=oracle.round_bf16)
+    ref = _block_loops(x, w_in, w_out, dirs, groups, cpw, rnd=_bf16_scalar)
+    np.testing.assert_allclose(z, ref, rtol=1e-11, atol=1e-12)
+    # the rounding is really applied, at both places
+    exact = oracle.block_fwd(x, w_in, w_out, dirs=dirs, groups=groups, cpw=cpw)
+    assert np.abs(z - exact).max() > 1e-4
+    gen_only = _block_loops(x, w_in, w_out, dirs, groups, cpw, rnd=None)
+    assert np.abs(gen_only - ref).max() > 1e-4
