@@ -15,10 +15,14 @@ synchronisations.  The steps rotate over R input/output buffer sets whose
 total footprint exceeds 512 MB, so the 256 MB Infinity Cache cannot serve a
 step's inputs from the previous step; a same-buffer ("hot") figure is
 reported separately.  The K timed steps run back to back (the throughput
-`value`); then the same K steps run again with each launch bracketed by HIP
-events on the stream it runs on (the per-launch durations of the roofline
-figure).  The plain forward and backward steps call the C ABI directly with
-argument tuples built once.
+`value`).  Then a roofline pass, whose length does not depend on K: 20 more
+untimed steps, then 200 steps each bracketed by HIP events on the stream the
+kernels run on; roofline.achieved is the algorithmic bytes over the median
+of those 200 durations.  `--profile-run` stops after the roofline pass (no
+hot pass, copy or CPU leg), and `--summarize-trace` turns the rocprofv3
+kernel trace of such a run into the committed kernel-time summary over the
+same 200 steps.  The plain forward and backward steps call the C ABI
+directly with argument tuples built once.
 
 device_copy_gbps: a plain 512 MiB device-to-device copy on the same GPU
 (read + write bytes per second), the practical streaming ceiling, for context.
@@ -67,6 +71,9 @@ METRIC_BWD = "GSPN scan backward GB/s and % of HBM peak (4-dir bwd)"
 METRIC_DIRS = "GSPN scan GB/s and % of HBM peak (4-dir fwd, per-direction lambda and u)"
 METRIC_BWD_DIRS = "GSPN scan backward GB/s and % of HBM peak (4-dir bwd, per-direction lambda and u)"
 HBM_PEAK_GBPS = 8000.0
+# roofline pass: untimed launches, then launches each timed with an event pair
+ROOF_WARM, ROOF_N = 20, 200
+HOT_N = 50
 COPY_CALIBRATION_BYTES = 256 * 1024 * 1024
 # The dominant kernel of each pass on the default workload (C-GSPN 1K, 64 x 64
 # grids: one fused kernel per call), the sources its code comes from, and its
@@ -238,9 +245,75 @@ def summarize_stats(stats_csv, command, config="cgspn1k", pass_="fwd", name=None
     print("\n".join(lines))
 
 
-def cpu_baseline(cfg_name: str, budget_s: float = 8.0, backward: bool = False):
-    """Time the fp64 oracle on a bounded sample of the same workload: whole
-    batch items, repeated until about budget_s seconds of wall time."""
+GSPN_KERNELS = ("fused_scan_kernel", "fused_scan_batched_kernel", "fused_bwd_kernel", "adjoint_scan_kernel",
+                "line_scan_kernel", "transpose_kernel", "convert_kernel", "merge_kernel", "merge_dirs_kernel",
+                "direction_kernel")
+
+
+def summarize_trace(trace_csv, command, config, pass_, warmup, steps, name=None):
+    """Kernel-time summary of a `--profile-run` bench under rocprofv3
+    --kernel-trace: the library's dispatches of the roofline pass only (the
+    last ROOF_N steps of the run; warm-up, timed steps and the roofline
+    pass's own warm-up are skipped), per kernel and per step."""
+    import csv
+    import numpy as np
+    from linear_spatial_propagation_amd.inputs import CONFIGS
+    rows = [r for r in csv.DictReader(open(trace_csv))
+            if any(k in r["Kernel_Name"] for k in GSPN_KERNELS)]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    total_steps = warmup + steps + ROOF_WARM + ROOF_N
+    if len(rows) % total_steps:
+        raise SystemExit(f"{len(rows)} library dispatches do not divide into {total_steps} steps")
+    per_step = len(rows) // total_steps
+    sel = rows[-ROOF_N * per_step:]
+    dur = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel], dtype=np.float64)
+    step_ns = dur.reshape(ROOF_N, per_step).sum(axis=1)
+    c = CONFIGS[config]
+    alg = (algorithmic_bytes_bwd if pass_ == "bwd" else algorithmic_bytes)(
+        c["B"], c["C"], c["H"], c["W"], 15, c["groups"], c["cpw"], c["dtype"])
+    lines = [f"# rocprofv3 --kernel-trace summary, workload {config} ({pass_}), roofline pass only:",
+             f"# the last {ROOF_N} steps of the run, after {warmup} warm-up, {steps} timed and {ROOF_WARM} more "
+             f"untimed steps; {per_step} library dispatch(es) per step",
+             f"# command: {command}",
+             "kernel, dispatches, average_ns, median_ns, min_ns, max_ns"]
+    names = [_kernel_short(r["Kernel_Name"]) for r in sel]
+    for k in dict.fromkeys(names):
+        d = np.array([v for v, n in zip(dur, names) if n == k])
+        lines.append(f"{k}, {len(d)}, {d.mean():.1f}, {np.median(d):.1f}, {d.min():.0f}, {d.max():.0f}")
+    med = float(np.median(step_ns))
+    lines += [f"step_kernel_ns_average: {step_ns.mean():.1f}",
+              f"step_kernel_ns_median: {med:.1f}",
+              f"step_kernel_ns_p10: {np.percentile(step_ns, 10):.1f}",
+              f"step_kernel_ns_p90: {np.percentile(step_ns, 90):.1f}",
+              f"algorithmic_bytes_per_step: {alg}",
+              f"achieved_gbps_at_median: {alg / med:.1f}",
+              f"frac_of_8000_gbps_at_median: {alg / med / HBM_PEAK_GBPS:.4f}"]
+    if name is None and config == "cgspn1k":
+        lines.append(f"kernel_source_hash: {kernel_source_hash(pass_)}")
+    stem = name or PASSES[pass_]["kernel"]
+    out = os.path.join(ROOT, "profiles", f"{stem}_{config}_stats.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg_name: str, budget_s: float = 4.0, backward: bool = False):
+    """Time the fp64 oracle, as it stands, on a bounded sample of the same
+    workload: whole batch items.  Three runs with every thread the oracle
+    gets (each repeats the sample for about budget_s seconds; the median run
+    is the value), then three runs on one thread over a smaller sample."""
+    import numpy as np
     import oracle
     from linear_spatial_propagation_amd.inputs import CONFIGS, gy_f64, make_gy, make_workload
 
@@ -256,27 +329,38 @@ def cpu_baseline(cfg_name: str, budget_s: float = 8.0, backward: bool = False):
             args += (gy_f64(make_gy(wl, 1000 + cfg["seed"]), wl.dtype),)
         return wl, args
 
-    def run(wl, args):
+    def once(wl, args, nthreads):
         t0 = time.perf_counter()
         fn = oracle.scan_bwd if backward else oracle.scan_fwd
-        fn(*args, dirs=15, groups=wl.groups, cpw=wl.cpw, nthreads=threads)
+        fn(*args, dirs=15, groups=wl.groups, cpw=wl.cpw, nthreads=nthreads)
         return time.perf_counter() - t0
 
-    wl, args = prepare(1)
-    t1 = run(wl, args)
-    nb = int(max(1, min(B, budget_s / 4 / max(t1, 1e-6))))
-    if nb > 1:
+    def rate(nb, nthreads, t_single):
+        """Median over three runs of GB/s; each run repeats the sample for
+        about budget_s / 3 seconds."""
         wl, args = prepare(nb)
-    reps, total = 0, 0.0
-    while total < budget_s and reps < 1000:
-        total += run(wl, args)
-        reps += 1
-    t = total / reps
-    nbytes = (algorithmic_bytes_bwd if backward else algorithmic_bytes)(
-        nb, C, H, W, 15, cfg["groups"], cfg["cpw"], cfg["dtype"])
-    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{nb} of {B} batch items ({nb * C} (b,c) slices) of the same workload, "
-                      f"fp64 C oracle with OpenMP over slices, mean of {reps} runs of {t:.3f} s"}
+        nbytes = (algorithmic_bytes_bwd if backward else algorithmic_bytes)(
+            nb, C, H, W, 15, cfg["groups"], cfg["cpw"], cfg["dtype"])
+        reps = max(1, int(budget_s / 3 / max(t_single, 1e-6)))
+        runs = []
+        for _ in range(3):
+            t = sum(once(wl, args, nthreads) for _ in range(reps)) / reps
+            runs.append(nbytes / t / 1e9)
+        return float(np.median(runs)), reps
+
+    wl1, args1 = prepare(1)
+    t1 = once(wl1, args1, threads)                  # one batch item, every thread
+    nb = int(max(1, min(B, budget_s / 6 / max(t1, 1e-6))))
+    all_threads, reps = rate(nb, threads, t1 * nb)
+    t1s = once(wl1, args1, 1)                       # one batch item, one thread
+    nb1 = int(max(1, min(B, budget_s / 6 / max(t1s, 1e-6))))
+    one_thread, reps1 = rate(nb1, 1, t1s * nb1)
+    return {"value": round(all_threads, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "one_thread_value": round(one_thread, 4),
+            "sample": f"{nb} of {B} batch items ({nb * C} (b,c) slices) of the same workload, fp64 C oracle "
+                      f"with OpenMP over slices on {threads} threads, median of 3 runs of {reps} repeats; "
+                      f"one thread: {nb1} batch item(s), median of 3 runs of {reps1} repeats"}
 
 
 def bench_block(args):
@@ -374,6 +458,9 @@ def main():
     ap.add_argument("--block", action="store_true",
                     help="time the compressed block (gspn_block_fwd) on the 1K block workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="warm-up, timed steps and the roofline pass only (no hot pass, copy or CPU leg): "
+                         "the run a kernel-trace summary is taken from")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for counter calibration)")
     ap.add_argument("--summarize-pmc", metavar="DIR",
@@ -383,9 +470,16 @@ def main():
     ap.add_argument("--summarize-stats", metavar="CSV",
                     help="write the kernel-time summary from a rocprofv3 --stats CSV and exit")
     ap.add_argument("--profile-command", default="", help="command line recorded in the summary")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="write the kernel-time summary of a --profile-run from its rocprofv3 kernel-trace CSV "
+                         "(give the run's --steps and --warmup) and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.profile_command, args.config, args.pass_)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.profile_command, args.config, args.pass_, args.warmup,
+                        args.steps, args.profile_name)
         return
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, args.profile_command, args.config, args.pass_,
@@ -529,11 +623,14 @@ def main():
     wall = time.perf_counter() - w0
     elapsed = t_all0.elapsed_time(t_all1) * 1e-3
 
-    # the same K steps again with an event pair around each launch: the
-    # per-launch durations of the roofline figure
+    # roofline pass, independent of K: ROOF_WARM more untimed launches, then
+    # ROOF_N launches each bracketed by an event pair on the launch stream;
+    # roofline.achieved uses the median duration (rotating buffers as above)
+    for i in range(ROOF_WARM):
+        step(i)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for i in range(args.steps):
+          for _ in range(ROOF_N)]
+    for i in range(ROOF_N):
         ev[i][0].record(stream)
         step(i)
         ev[i][1].record(stream)
@@ -541,14 +638,16 @@ def main():
     per = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3   # s per launch
 
     # same-buffer ("hot") figure: the Infinity Cache may serve the inputs
-    hot_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(min(args.steps, 200))]
-    for a, b in hot_ev:
-        a.record(stream)
-        step(0)
-        b.record(stream)
-    torch.cuda.synchronize(dev)
-    hot = np.array([a.elapsed_time(b) for a, b in hot_ev]) * 1e-3
+    hot = None
+    if not args.profile_run:
+        hot_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(HOT_N)]
+        for a, b in hot_ev:
+            a.record(stream)
+            step(0)
+            b.record(stream)
+        torch.cuda.synchronize(dev)
+        hot = np.array([a.elapsed_time(b) for a, b in hot_ev]) * 1e-3
 
     separate_us = None
     if batched > 1:
@@ -570,7 +669,7 @@ def main():
     # practical ceiling, for context: a plain device-to-device copy of
     # 2 x 512 MiB buffers (read + write bytes per second), median of 20
     copy_gbps = None
-    if batched == 1 and not args.copy_calibration:   # the counter runs keep one known copy
+    if batched == 1 and not args.copy_calibration and not args.profile_run:   # the counter runs keep one known copy
         csrc = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
         cdst = torch.empty_like(csrc)
         cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
@@ -585,8 +684,8 @@ def main():
 
     ms_per_step = elapsed / args.steps * 1e3
     value = nbytes * args.steps / elapsed / 1e9
-    avg_launch = float(per.mean())
-    achieved = nbytes / avg_launch / 1e9
+    med_launch = float(np.median(per))
+    achieved = nbytes / med_launch / 1e9
     traffic = load_traffic(args.pass_) if args.config == "cgspn1k" and args.variant == "none" else None
     E = B * C * H * W
     out = {
@@ -600,7 +699,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": f"{wl.dtype} I/O, f32 arithmetic",
         "data": "synthetic",
         "config": {
             "workload": f"{args.config}: B={B} C={C} H={H} W={W} groups={wl.groups} "
@@ -617,10 +716,11 @@ def main():
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "elements_per_s": round(E * batched * args.steps / elapsed, 1),
-        "launch_us": {"mean": round(avg_launch * 1e6, 3), "p10": round(float(np.percentile(per, 10)) * 1e6, 3),
-                      "median": round(float(np.median(per)) * 1e6, 3),
+        "launch_us": {"launches": ROOF_N, "mean": round(float(per.mean()) * 1e6, 3),
+                      "p10": round(float(np.percentile(per, 10)) * 1e6, 3),
+                      "median": round(med_launch * 1e6, 3),
                       "p90": round(float(np.percentile(per, 90)) * 1e6, 3)},
-        "hot_cache_gbps": round(nbytes / float(np.median(hot)) / 1e9, 2),
+        "hot_cache_gbps": round(nbytes / float(np.median(hot)) / 1e9, 2) if hot is not None else None,
         "device_copy_gbps": copy_gbps,
         "wall_s": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -640,7 +740,7 @@ def main():
         out["roofline"]["kernel"] = ("gspn_scan_bwd_ex, all launches of one call" if bwd_variant else
                                      "fused_bwd_kernel" if max(H, W) <= 64
                                      else "gspn_scan_bwd, all launches of one call")
-    if not args.no_cpu and args.variant == "none" and batched == 1:
+    if not args.no_cpu and not args.profile_run and args.variant == "none" and batched == 1:
         out["cpu_baseline"] = cpu_baseline(args.config, backward=bwd)
     print(json.dumps(out), flush=True)
 
