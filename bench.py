@@ -71,7 +71,7 @@ METRIC_BWD = "GSPN scan backward GB/s and % of HBM peak (4-dir bwd)"
 METRIC_DIRS = "GSPN scan GB/s and % of HBM peak (4-dir fwd, per-direction lambda and u)"
 METRIC_BWD_DIRS = "GSPN scan backward GB/s and % of HBM peak (4-dir bwd, per-direction lambda and u)"
 HBM_PEAK_GBPS = 8000.0
-# roofline pass: untimed launches, then launches each timed with an event pair
+# steady-state pass after the timed region: untimed steps, then steps back to back
 ROOF_WARM, ROOF_N = 20, 200
 HOT_N = 50
 COPY_CALIBRATION_BYTES = 256 * 1024 * 1024
@@ -148,28 +148,27 @@ def load_traffic(pass_="fwd"):
 
 
 def _kernel_short(name):
-    for k in ("fused_scan_kernel", "fused_bwd_kernel", "adjoint_scan_kernel", "line_scan_kernel",
-              "transpose_kernel", "convert_kernel"):
+    """Short kernel name (the template arguments dropped)."""
+    for k in ("fused_scan_batched_kernel", "fused_scan_kernel", "fused_bwd_kernel", "adjoint_scan_kernel",
+              "line_scan_kernel", "transpose_kernel", "convert_kernel", "merge_dirs_kernel", "merge_kernel",
+              "direction_kernel"):
         if k in name:
             return k
-    if "fused_scan_kernel" in name:
-        return "fused_scan_kernel"
-    if "direction_kernel" in name:
-        return "direction_kernel"
-    if "merge_kernel" in name:
-        return "merge_kernel"
     if "copyBuffer" in name:
         return "copy"
     return name[:48]
 
 
-def summarize_pmc(pmc_dir, command, config="cgspn1k", pass_="fwd"):
+def summarize_pmc(pmc_dir, command, config="cgspn1k", pass_="fwd", name=None):
     """Summarise two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) of a bench
     run with --copy-calibration into the traffic summary under profiles/.
 
     FETCH_SIZE / WRITE_SIZE are KiB per dispatch.  Each is scaled by the
     ratio between the known size of the plain device copy (256 MiB read,
-    256 MiB written) and what the same counter reads for that copy."""
+    256 MiB written) and what the same counter reads for that copy.  A step
+    may run several of the library's kernels (the line path); the bytes of
+    one step are the sum over its dispatches, and the number of steps is the
+    number of dispatches of the step's anchor kernel (run once per step)."""
     import csv
     import glob
     from linear_spatial_propagation_amd.inputs import CONFIGS
@@ -180,8 +179,11 @@ def summarize_pmc(pmc_dir, command, config="cgspn1k", pass_="fwd"):
             per.setdefault(key, [row["Kernel_Name"], 0.0])
             per[key][1] += float(row["Counter_Value"])
     vals = {}
-    for (counter, did), (name, v) in per.items():
-        vals.setdefault((counter, _kernel_short(name)), []).append((did, v))
+    for (counter, did), (kname_full, v) in per.items():
+        short = "copy" if "copyBuffer" in kname_full else (
+            _kernel_short(kname_full) if any(k in kname_full for k in GSPN_KERNELS) else None)
+        if short:
+            vals.setdefault((counter, short), []).append((did, v))
     copy_w = max(v for _, v in vals[("WRITE_SIZE", "copy")])
     copy_w_id = [d for d, v in vals[("WRITE_SIZE", "copy")] if v == copy_w][0]
     copy_f = dict(vals[("FETCH_SIZE", "copy")]).get(copy_w_id)
@@ -189,24 +191,34 @@ def summarize_pmc(pmc_dir, command, config="cgspn1k", pass_="fwd"):
         copy_f = max(v for _, v in vals[("FETCH_SIZE", "copy")])
     copy_kib = COPY_CALIBRATION_BYTES / 1024
     f_scale, w_scale = copy_kib / copy_f, copy_kib / copy_w
-    kname = PASSES[pass_]["kernel"]
-    fk = [v for _, v in vals[("FETCH_SIZE", kname)]]
-    wk = [v for _, v in vals[("WRITE_SIZE", kname)]]
-    fetch_kib, write_kib = sum(fk) / len(fk), sum(wk) / len(wk)
-    hbm = fetch_kib * 1024 * f_scale + write_kib * 1024 * w_scale
     c = CONFIGS[config]
+    lines_path = max(c["H"], c["W"]) > 64
+    anchor = ("adjoint_scan_kernel" if lines_path else "fused_bwd_kernel") if pass_ == "bwd" else (
+        "line_scan_kernel" if lines_path else "fused_scan_kernel")
+    kernels = sorted({k for (_, k) in vals if k != "copy"})
+    steps = len(vals[("FETCH_SIZE", anchor)])
+    fetch_kib = sum(v for k in kernels for _, v in vals.get(("FETCH_SIZE", k), [])) / steps
+    write_kib = sum(v for k in kernels for _, v in vals.get(("WRITE_SIZE", k), [])) / steps
+    hbm = fetch_kib * 1024 * f_scale + write_kib * 1024 * w_scale
     alg = (algorithmic_bytes_bwd if pass_ == "bwd" else algorithmic_bytes)(
         c["B"], c["C"], c["H"], c["W"], 15, c["groups"], c["cpw"], c["dtype"])
     lines = [
-        f"# rocprofv3 memory counters: {kname}<bf16> on {config} "
+        f"# rocprofv3 memory counters: {pass_} step on {config} "
         f"(B={c['B']} C={c['C']} H={c['H']} W={c['W']} groups={c['groups']} ch_per_weight={c['cpw']} {c['dtype']})",
         f"# command (two passes, FETCH_SIZE then WRITE_SIZE): {command}",
-        "# FETCH_SIZE and WRITE_SIZE are KiB per dispatch, averaged over the kernel's dispatches;",
+        "# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; a step's bytes are the sum over its dispatches;",
         "# each is scaled by (known bytes / counter bytes) of a 256 MiB device-to-device copy in the same run.",
-        f"kernel_source_hash: {kernel_source_hash(pass_)}",
-        f"dispatches: {len(fk)}",
-        f"fetch_kib_per_dispatch: {fetch_kib:.1f}",
-        f"write_kib_per_dispatch: {write_kib:.1f}",
+    ]
+    if not lines_path:
+        lines.append(f"kernel_source_hash: {kernel_source_hash(pass_)}")
+    lines += [f"steps: {steps}", f"kernels_per_step: {', '.join(kernels)}"]
+    for k in kernels:
+        fk = sum(v for _, v in vals.get(("FETCH_SIZE", k), [])) / steps
+        wk = sum(v for _, v in vals.get(("WRITE_SIZE", k), [])) / steps
+        lines.append(f"  {k}: read {fk * 1024 * f_scale / 1e6:.1f} MB, write {wk * 1024 * w_scale / 1e6:.1f} MB per step")
+    lines += [
+        f"fetch_kib_per_step: {fetch_kib:.1f}",
+        f"write_kib_per_step: {write_kib:.1f}",
         f"copy_known_bytes: {COPY_CALIBRATION_BYTES}",
         f"copy_fetch_kib: {copy_f:.1f}",
         f"copy_write_kib: {copy_w:.1f}",
@@ -218,7 +230,8 @@ def summarize_pmc(pmc_dir, command, config="cgspn1k", pass_="fwd"):
         f"algorithmic_bytes_per_launch: {alg}",
         f"traffic_over_algorithmic: {hbm / alg:.4f}",
     ]
-    with open(profile_path(pass_, "traffic", config), "w") as f:
+    stem = name or PASSES[pass_]["kernel"]
+    with open(os.path.join(ROOT, "profiles", f"{stem}_{config}_traffic.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -252,9 +265,10 @@ GSPN_KERNELS = ("fused_scan_kernel", "fused_scan_batched_kernel", "fused_bwd_ker
 
 def summarize_trace(trace_csv, command, config, pass_, warmup, steps, name=None):
     """Kernel-time summary of a `--profile-run` bench under rocprofv3
-    --kernel-trace: the library's dispatches of the roofline pass only (the
-    last ROOF_N steps of the run; warm-up, timed steps and the roofline
-    pass's own warm-up are skipped), per kernel and per step."""
+    --kernel-trace: the library's dispatches of the timed region (the K steps
+    after the W warm-up steps, whose event-timed average gives
+    roofline.achieved), per kernel and per step, and of the steady-state
+    pass that follows it."""
     import csv
     import numpy as np
     from linear_spatial_propagation_amd.inputs import CONFIGS
@@ -265,29 +279,36 @@ def summarize_trace(trace_csv, command, config, pass_, warmup, steps, name=None)
     if len(rows) % total_steps:
         raise SystemExit(f"{len(rows)} library dispatches do not divide into {total_steps} steps")
     per_step = len(rows) // total_steps
-    sel = rows[-ROOF_N * per_step:]
-    dur = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel], dtype=np.float64)
-    step_ns = dur.reshape(ROOF_N, per_step).sum(axis=1)
     c = CONFIGS[config]
     alg = (algorithmic_bytes_bwd if pass_ == "bwd" else algorithmic_bytes)(
         c["B"], c["C"], c["H"], c["W"], 15, c["groups"], c["cpw"], c["dtype"])
-    lines = [f"# rocprofv3 --kernel-trace summary, workload {config} ({pass_}), roofline pass only:",
-             f"# the last {ROOF_N} steps of the run, after {warmup} warm-up, {steps} timed and {ROOF_WARM} more "
-             f"untimed steps; {per_step} library dispatch(es) per step",
-             f"# command: {command}",
-             "kernel, dispatches, average_ns, median_ns, min_ns, max_ns"]
-    names = [_kernel_short(r["Kernel_Name"]) for r in sel]
-    for k in dict.fromkeys(names):
-        d = np.array([v for v, n in zip(dur, names) if n == k])
-        lines.append(f"{k}, {len(d)}, {d.mean():.1f}, {np.median(d):.1f}, {d.min():.0f}, {d.max():.0f}")
-    med = float(np.median(step_ns))
-    lines += [f"step_kernel_ns_average: {step_ns.mean():.1f}",
-              f"step_kernel_ns_median: {med:.1f}",
-              f"step_kernel_ns_p10: {np.percentile(step_ns, 10):.1f}",
-              f"step_kernel_ns_p90: {np.percentile(step_ns, 90):.1f}",
-              f"algorithmic_bytes_per_step: {alg}",
-              f"achieved_gbps_at_median: {alg / med:.1f}",
-              f"frac_of_8000_gbps_at_median: {alg / med / HBM_PEAK_GBPS:.4f}"]
+    lines = [f"# rocprofv3 --kernel-trace summary, workload {config} ({pass_}); {per_step} library dispatch(es) "
+             "per step",
+             f"# timed region: steps {warmup}..{warmup + steps - 1} (after {warmup} warm-up steps); steady state: "
+             f"the {ROOF_N} steps after {ROOF_WARM} more untimed ones",
+             f"# command: {command}"]
+
+    def part(label, first, count):
+        sel = rows[first * per_step:(first + count) * per_step]
+        dur = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel], dtype=np.float64)
+        span = (int(sel[-1]["End_Timestamp"]) - int(sel[0]["Start_Timestamp"])) / count
+        step_ns = dur.reshape(count, per_step).sum(axis=1)
+        names = [_kernel_short(r["Kernel_Name"]) for r in sel]
+        out = [f"[{label}] kernel, dispatches, average_ns, median_ns, min_ns, max_ns"]
+        for k in dict.fromkeys(names):
+            d = np.array([v for v, n in zip(dur, names) if n == k])
+            out.append(f"{k}, {len(d)}, {d.mean():.1f}, {np.median(d):.1f}, {d.min():.0f}, {d.max():.0f}")
+        avg = float(step_ns.mean())
+        out += [f"{label}_step_kernel_ns_average: {avg:.1f}",
+                f"{label}_step_kernel_ns_median: {np.median(step_ns):.1f}",
+                f"{label}_first_start_to_last_end_ns_per_step: {span:.1f}",
+                f"{label}_achieved_gbps_at_average: {alg / avg:.1f}",
+                f"{label}_frac_of_8000_gbps_at_average: {alg / avg / HBM_PEAK_GBPS:.4f}"]
+        return out
+
+    lines += part("timed", warmup, steps)
+    lines += part("steady", warmup + steps + ROOF_WARM, ROOF_N)
+    lines.append(f"algorithmic_bytes_per_step: {alg}")
     if name is None and config == "cgspn1k":
         lines.append(f"kernel_source_hash: {kernel_source_hash(pass_)}")
     stem = name or PASSES[pass_]["kernel"]
@@ -475,7 +496,7 @@ def main():
                          "(give the run's --steps and --warmup) and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc, args.profile_command, args.config, args.pass_)
+        summarize_pmc(args.summarize_pmc, args.profile_command, args.config, args.pass_, args.profile_name)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.profile_command, args.config, args.pass_, args.warmup,
@@ -623,19 +644,19 @@ def main():
     wall = time.perf_counter() - w0
     elapsed = t_all0.elapsed_time(t_all1) * 1e-3
 
-    # roofline pass, independent of K: ROOF_WARM more untimed launches, then
-    # ROOF_N launches each bracketed by an event pair on the launch stream;
-    # roofline.achieved uses the median duration (rotating buffers as above)
+    # steady-state pass, independent of K: ROOF_WARM more untimed steps,
+    # then ROOF_N steps back to back between one event pair (reported
+    # beside the timed region; not the `value`)
     for i in range(ROOF_WARM):
         step(i)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(ROOF_N)]
+    st0 = torch.cuda.Event(enable_timing=True)
+    st1 = torch.cuda.Event(enable_timing=True)
+    st0.record(stream)
     for i in range(ROOF_N):
-        ev[i][0].record(stream)
         step(i)
-        ev[i][1].record(stream)
+    st1.record(stream)
     torch.cuda.synchronize(dev)
-    per = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3   # s per launch
+    steady = st0.elapsed_time(st1) * 1e-3 / ROOF_N
 
     # same-buffer ("hot") figure: the Infinity Cache may serve the inputs
     hot = None
@@ -684,8 +705,9 @@ def main():
 
     ms_per_step = elapsed / args.steps * 1e3
     value = nbytes * args.steps / elapsed / 1e9
-    med_launch = float(np.median(per))
-    achieved = nbytes / med_launch / 1e9
+    # roofline: algorithmic bytes over the average step of the timed region
+    # (HIP events on the launch stream around the K back-to-back steps)
+    achieved = nbytes / (elapsed / args.steps) / 1e9
     traffic = load_traffic(args.pass_) if args.config == "cgspn1k" and args.variant == "none" else None
     E = B * C * H * W
     out = {
@@ -716,10 +738,9 @@ def main():
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "elements_per_s": round(E * batched * args.steps / elapsed, 1),
-        "launch_us": {"launches": ROOF_N, "mean": round(float(per.mean()) * 1e6, 3),
-                      "p10": round(float(np.percentile(per, 10)) * 1e6, 3),
-                      "median": round(med_launch * 1e6, 3),
-                      "p90": round(float(np.percentile(per, 90)) * 1e6, 3)},
+        "step_us": round(elapsed / args.steps * 1e6, 3),
+        "steady_state": {"steps": ROOF_N, "after_warmup": ROOF_WARM, "step_us": round(steady * 1e6, 3),
+                         "gbps": round(nbytes / steady / 1e9, 2)},
         "hot_cache_gbps": round(nbytes / float(np.median(hot)) / 1e9, 2) if hot is not None else None,
         "device_copy_gbps": copy_gbps,
         "wall_s": round(wall, 4),
