@@ -110,7 +110,8 @@ enum {
     GSPN_ERR_ALIAS = -8,  /* an output overlaps an input or another output */
     GSPN_ERR_HIP = -9,    /* a HIP call failed; see gspn_last_error() */
     GSPN_ERR_PATH = -10,  /* unknown path, or the path (or the backward) cannot take this shape */
-    GSPN_ERR_FLAGS = -11  /* unknown bit in flags (gspn_scan_fwd_ex, gspn_scan_bwd_ex) */
+    GSPN_ERR_FLAGS = -11, /* unknown bit in flags (gspn_scan_fwd_ex, gspn_scan_bwd_ex) */
+    GSPN_ERR_SCRATCH = -12 /* the shape's workspace exceeds GSPN_NOALLOC_SCRATCH_BYTES (gspn_scan_fwd_noalloc) */
 };
 
 /* Flags of gspn_scan_fwd_ex and gspn_scan_bwd_ex. */
@@ -145,6 +146,29 @@ enum {
 int gspn_scan_fwd(const void *x, const void *w_raw, const void *lam, const void *u, void *y,
                   int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
                   int32_t ch_per_weight, int32_t dtype, hipStream_t stream);
+
+/*
+ * gspn_scan_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same operation, arguments, layouts and errors as gspn_scan_fwd, and the
+ * same kernels.  It calls no hipMalloc, hipFree or allocating library
+ * routine: where gspn_scan_fwd takes a stream-ordered workspace (shapes with
+ * H or W above 64), this entry point uses a static device array of
+ * GSPN_NOALLOC_SCRATCH_BYTES, one per GPU, held until the process ends;
+ * shapes with H, W <= 64 need none.  A shape whose workspace (the formula
+ * above) is larger returns GSPN_ERR_SCRATCH before anything is enqueued.
+ * Every call on one GPU shares that GPU's array and leaves it holding that
+ * call's intermediates (nothing in it needs to start at zero): calls that
+ * overlap on one GPU (on different streams or threads) race on it and must
+ * be serialised by the caller.  The first call on a device, made with that
+ * device current, looks up the array's device address (hipGetSymbolAddress;
+ * GSPN_ERR_HIP if that fails) and keeps it for later calls.
+ */
+#define GSPN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int gspn_scan_fwd_noalloc(const void *x, const void *w_raw, const void *lam, const void *u, void *y,
+                          int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
+                          int32_t ch_per_weight, int32_t dtype, hipStream_t stream);
 
 /* Same operation on a chosen kernel path (GSPN_PATH_*); used to cross-check
  * the paths against each other.  GSPN_ERR_PATH if the path cannot run the

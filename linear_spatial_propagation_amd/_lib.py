@@ -22,6 +22,8 @@ DIR_TB, DIR_BT, DIR_LR, DIR_RL, DIR_ALL = 1, 2, 4, 8, 15
 
 LAM_PER_DIR, U_PER_DIR = 1, 2
 MAX_BATCH = 32
+NOALLOC_SCRATCH_BYTES = 64 << 20
+ERR_SCRATCH = -12
 
 
 class Problem(ctypes.Structure):
@@ -31,7 +33,7 @@ class Problem(ctypes.Structure):
                 ("C", ctypes.c_int64), ("H", ctypes.c_int64), ("W", ctypes.c_int64),
                 ("dirs", ctypes.c_uint32), ("groups", ctypes.c_int32), ("ch_per_weight", ctypes.c_int32)]
 
-EXPORTED = ("gspn_scan_fwd", "gspn_scan_fwd_path", "gspn_scan_fwd_ex", "gspn_scan_fwd_batched",
+EXPORTED = ("gspn_scan_fwd", "gspn_scan_fwd_noalloc", "gspn_scan_fwd_path", "gspn_scan_fwd_ex", "gspn_scan_fwd_batched",
             "gspn_select_path", "gspn_scan_bwd",
             "gspn_scan_bwd_path", "gspn_scan_bwd_ex", "gspn_bwd_supported", "gspn_block_fwd", "gspn_block_rows",
             "gspn_status_string", "gspn_last_error", "gspn_version")
@@ -58,6 +60,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib = ctypes.CDLL(path)
         vp, i64, u32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int32
         lib.gspn_scan_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, u32, i32, i32, i32, vp]
+        lib.gspn_scan_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, u32, i32, i32, i32, vp]
+        lib.gspn_scan_fwd_noalloc.restype = ctypes.c_int
         lib.gspn_scan_fwd.restype = ctypes.c_int
         lib.gspn_scan_fwd_path.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, u32, i32, i32, i32,
                                            i32, vp]
@@ -108,6 +112,13 @@ def scan_fwd_ptr(x: int, w: int, lam: int, u: int, y: int, B: int, C: int, H: in
     """Raw call on device pointers; returns the status code."""
     return load().gspn_scan_fwd_path(x, w, lam, u, y, B, C, H, W, dirs, groups, ch_per_weight,
                                      dtype, path, stream)
+
+
+def scan_fwd_noalloc_ptr(x: int, w: int, lam: int, u: int, y: int, B: int, C: int, H: int, W: int, *,
+                         dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1, dtype: int = GSPN_BF16,
+                         stream: int = 0) -> int:
+    """Raw call of the allocation-free forward on device pointers; returns the status code."""
+    return load().gspn_scan_fwd_noalloc(x, w, lam, u, y, B, C, H, W, dirs, groups, ch_per_weight, dtype, stream)
 
 
 def scan_fwd_ex_ptr(x: int, w: int, lam: int, u: int, y: int, B: int, C: int, H: int, W: int, *,

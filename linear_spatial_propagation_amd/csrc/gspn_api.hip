@@ -73,6 +73,7 @@ const char* gspn_status_string(int status) {
         case GSPN_ERR_HIP: return "GSPN_ERR_HIP: a HIP call failed (see gspn_last_error)";
         case GSPN_ERR_PATH: return "GSPN_ERR_PATH: unknown path, or the path cannot run this shape";
         case GSPN_ERR_FLAGS: return "GSPN_ERR_FLAGS: unknown bit in flags";
+        case GSPN_ERR_SCRATCH: return "GSPN_ERR_SCRATCH: the shape's workspace exceeds the static scratch";
         default: return "unknown GSPN status";
     }
 }
@@ -149,9 +150,12 @@ int scan_bwd_impl(const void* x, const void* w_raw, const void* lam, const void*
 }
 
 
+// `scratch` (may be null): a device buffer of GSPN_NOALLOC_SCRATCH_BYTES that
+// serves as the workspace instead of a stream-ordered allocation; shapes whose
+// workspace is larger are rejected with GSPN_ERR_SCRATCH before any launch.
 int scan_fwd_impl(const void* x, const void* w_raw, const void* lam, const void* u, void* y, int64_t B,
                   int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups, int32_t ch_per_weight,
-                  uint32_t flags, int32_t dtype, int32_t path, hipStream_t stream) {
+                  uint32_t flags, int32_t dtype, int32_t path, hipStream_t stream, void* scratch = nullptr) {
     g_last_error[0] = '\0';
     int rc = check_sizes(B, C, H, W, dirs, groups, ch_per_weight, dtype);
     if (rc) return rc;
@@ -194,6 +198,18 @@ int scan_fwd_impl(const void* x, const void* w_raw, const void* lam, const void*
     // allow, else the per-line fallback)
     const bool lines = gspn::lines_supported(a.H, a.W);
     const size_t pbytes = lines ? gspn::lines_workspace_bytes(a) : (size_t)popcount4(dirs) * E * sizeof(float);
+    if (scratch) {
+        if (pbytes > (size_t)GSPN_NOALLOC_SCRATCH_BYTES) {
+            snprintf(g_last_error, sizeof(g_last_error),
+                     "the workspace of this shape (%zu bytes) exceeds the static scratch (%zu bytes)", pbytes,
+                     (size_t)GSPN_NOALLOC_SCRATCH_BYTES);
+            return GSPN_ERR_SCRATCH;
+        }
+        const hipError_t el = lines ? gspn::launch_lines(a, scratch, stream)
+                                    : gspn::launch_general(a, static_cast<float*>(scratch), stream);
+        if (el != hipSuccess) { set_error("general kernel launch", el); return GSPN_ERR_HIP; }
+        return GSPN_OK;
+    }
     void* work = nullptr;
     hipError_t e = hipMallocAsync(&work, pbytes, stream);
     if (e != hipSuccess) { set_error("hipMallocAsync(workspace)", e); return GSPN_ERR_HIP; }
@@ -271,6 +287,56 @@ int gspn_scan_fwd(const void* x, const void* w_raw, const void* lam, const void*
                   int32_t ch_per_weight, int32_t dtype, hipStream_t stream) {
     return gspn_scan_fwd_path(x, w_raw, lam, u, y, B, C, H, W, dirs, groups, ch_per_weight, dtype,
                               GSPN_PATH_AUTO, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-allocation entry point
+// The workspace of gspn_scan_fwd_noalloc: one static array per GPU, held
+// until the process ends.  Host code never uses the array's name as an
+// address (on the host it is only a stand-in for the symbol); the device
+// address comes from hipGetSymbolAddress, looked up once per device on the
+// first call made with that device current.
+static __device__ __align__(256) unsigned char scratch[GSPN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) { set_error("hipGetDevice", e); return GSPN_ERR_HIP; }
+    if (dev < 0 || dev >= kMaxDevices) { set_error_text("device index out of range"); return GSPN_ERR_HIP; }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            set_error("hipGetSymbolAddress(scratch)", e != hipSuccess ? e : hipErrorInvalidSymbol);
+            return GSPN_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GSPN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gspn_scan_fwd_noalloc(const void* x, const void* w_raw, const void* lam, const void* u, void* y,
+                          int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
+                          int32_t ch_per_weight, int32_t dtype, hipStream_t stream) {
+    g_last_error[0] = '\0';
+    void* ws = nullptr;
+    const int rc = scratch_address(&ws);
+    if (rc) return rc;
+    return scan_fwd_impl(x, w_raw, lam, u, y, B, C, H, W, dirs, groups, ch_per_weight, 0u, dtype,
+                         GSPN_PATH_AUTO, stream, ws);
 }
 
 int gspn_bwd_supported(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
