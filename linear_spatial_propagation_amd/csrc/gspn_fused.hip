@@ -20,7 +20,10 @@
 //    rcp per pixel) into registers (64 lines x 2 taps; the middle tap is
 //    implied by the unit row sum) and reuses them for
 //    every channel of the weight set: the sigmoid work is shared by the
-//    channel group instead of being repeated per channel.
+//    channel group instead of being repeated per channel.  Row directions
+//    stage their taps in chunks of 16 rows; column directions of bf16 grids
+//    copy their whole tap block (whole 128-byte rows) straight into LDS and
+//    normalise it from there, so no 128-byte line is fetched in pieces.
 //  * lambda * x of the current channel is staged once in LDS as fp32
 //    (row pitch 65 floats), with 16-byte coalesced loads, and read by all
 //    four waves: row directions read LDS rows, column directions read LDS
@@ -446,9 +449,20 @@ __device__ __forceinline__ void fused_scan_body(const FusedParams& prm, const in
     constexpr int N = Vec<T>::N;                     // elements per 16-byte access
     constexpr int kMaxIt = kS * kS / (kThreads * N); // merge/staging iterations
     constexpr int kChunk = 16;
+    // bf16 rows of whole vectors: the column directions copy their raw taps
+    // straight into LDS in the prologue (see column_prologue below)
+    constexpr bool kColDirect = VEC && sizeof(T) == 2;
+    // that copy: 3 taps x 64 rows of 144 bytes (a 128-byte bf16 row + 16
+    // bytes of padding) per column direction, after the two row waves'
+    // fp32 staging regions
+    constexpr int kRowStageBytes = 2 * 3 * kChunk * kPitch * 4;
+    constexpr int kColRowBytes = 144;
+    constexpr int kColRegionBytes = 3 * kS * kColRowBytes;
+    constexpr int kLdsFloats = kColDirect ? (kRowStageBytes + 2 * kColRegionBytes) / 4 : 3 * kPlane;
+    static_assert(kLdsFloats >= 3 * kPlane, "the prologue's LDS also holds the three planes");
     // LDS: XL (lambda*x of the current channel, fp32) | P_row | P_col; the
     // tap staging of the prologue reuses the same space.
-    __shared__ __attribute__((aligned(16))) float lds[3 * kPlane];
+    __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
 
     const T* __restrict__ gx = static_cast<const T*>(prm.x);
     const T* __restrict__ gw = static_cast<const T*>(prm.w);
@@ -569,6 +583,76 @@ __device__ __forceinline__ void fused_scan_body(const FusedParams& prm, const in
         constexpr int kSlotStep = kSlots <= kChunk / 2 ? 2 : 1;   // odd lines when they fit
         static_assert(kSlots <= kChunk && kItems <= kSlots * kNCh, "issue slots");
         static_assert(kAhead > 1 || kSlots >= kLd, "chunk c + 1 is issued while chunk c is normalised");
+        // Column directions of bf16 rows (whole vectors): the wave copies all
+        // of its direction's raw taps (3 x 64 rows of 128 bytes) into LDS
+        // with direct global-to-LDS loads, 16 bytes per lane, whole 128-byte
+        // rows -- the chunks of 16 columns the row path uses would read each
+        // 128-byte line in four 32-byte pieces, at different times -- and
+        // then normalises 8 line coordinates (columns) per 16-byte LDS read
+        // of its own row (lane p = row p; the 144-byte row pitch keeps those
+        // reads free of bank conflicts).  Taps that are never used (outside
+        // the grid, a missing border tap, the scan's first line) are zeroed
+        // on the way into normalise_fast, as the row path's staging does.
+        auto column_prologue = [&]() {
+            constexpr int kBlocks = kColRegionBytes / 1024;   // 1 KB per wave-wide copy
+            static_assert(kColRegionBytes % 1024 == 0, "whole 1 KB blocks");
+            char* region = reinterpret_cast<char*>(lds) + kRowStageBytes + (d - 2) * kColRegionBytes;
+            if (on) {
+                const T* src = wsrc.dir(d);
+                const int vpr = W / N;   // 16-byte pieces per row
+#pragma unroll
+                for (int i = 0; i < kBlocks; ++i) {
+                    // 16-byte slot i*64 + p of the region: LDS row lr (tap
+                    // lr / 64, grid row lr % 64), piece kk of 9 (piece 8 is
+                    // padding and repeats piece 7); rows and pieces outside
+                    // the grid read clamped addresses and are masked below
+                    const int sl = i * 64 + p;
+                    const int lr = sl / 9, kk = sl - lr * 9;
+                    const T* g = src + (size_t)(lr >> 6) * HW + min(lr & 63, H - 1) * W + min(kk, vpr - 1) * N;
+#if defined(__HIP_DEVICE_COMPILE__)
+                    __builtin_amdgcn_global_load_lds(g, region + i * 1024, 16, 0, 0);
+#endif
+                }
+            }
+            load_rows(gx, c_begin, x1);
+            load_rows(glam, c_begin, l1);
+            load_rows(gu, c_begin, u0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies have landed in LDS
+            const bool has1 = p < m;
+            static_for<0, kS / 8>([&](auto gc) {
+                constexpr int g8 = decltype(gc)::value;
+                __builtin_amdgcn_sched_barrier(0);
+                float a0[8], a1[8], a2[8];
+                unpack(*reinterpret_cast<const uint4*>(region + (0 * kS + p) * kColRowBytes + g8 * 16), a0);
+                unpack(*reinterpret_cast<const uint4*>(region + (1 * kS + p) * kColRowBytes + g8 * 16), a1);
+                unpack(*reinterpret_cast<const uint4*>(region + (2 * kS + p) * kColRowBytes + g8 * 16), a2);
+                float amin = 0.0f;
+                static_for<0, 8>([&](auto ec) {
+                    constexpr int e = decltype(ec)::value;
+                    constexpr int j = g8 * 8 + e;   // line coordinate (column)
+                    const bool used = on && j < W && j != first_line;
+                    a0[e] = used && has0 ? a0[e] : 0.0f;
+                    a1[e] = used && has1 ? a1[e] : 0.0f;
+                    a2[e] = used && has2 ? a2[e] : 0.0f;
+                    amin = fminf(amin, fminf(fminf(a0[e], a1[e]), a2[e]));
+                    const float2 w = normalise_fast(a0[e], a1[e], a2[e], has0, has2);
+                    w0[j] = w.x;
+                    w2[j] = w.y;
+                });
+                // a tap below -40 in these 8 columns: the exact-form branches
+                if (__builtin_amdgcn_ballot_w64(amin < -40.0f) != 0) {
+                    static_for<0, 8>([&](auto ec) {
+                        constexpr int e = decltype(ec)::value;
+                        const Taps tp = normalise_taps(a0[e], a1[e], a2[e], has0, has2);
+                        w0[g8 * 8 + e] = tp.w0;
+                        w2[g8 * 8 + e] = tp.w2;
+                    });
+                }
+            });
+        };
+        // Row directions (and every direction of other instantiations):
+        // chunks of 16 line coordinates staged as fp32 in the wave's region.
+        auto chunked_prologue = [&]() {
         TapChunk<T> tapv[kNCh];
         if constexpr (VEC) {
 #pragma unroll
@@ -623,6 +707,9 @@ __device__ __forceinline__ void fused_scan_body(const FusedParams& prm, const in
                 });
             }
         });
+        };
+        if (kColDirect && d >= 2) column_prologue();
+        else chunked_prologue();
         __syncthreads();   // every wave is done with the staging area (it becomes XL)
     }
 
