@@ -151,7 +151,7 @@ def _kernel_short(name):
     """Short kernel name (the template arguments dropped)."""
     for k in ("fused_scan_batched_kernel", "fused_scan_kernel", "fused_bwd_kernel", "adjoint_scan_kernel",
               "line_scan_kernel", "transpose_kernel", "convert_kernel", "merge_dirs_kernel", "merge_kernel",
-              "direction_kernel"):
+              "direction_kernel", "outproj_kernel", "rms_scale_kernel"):
         if k in name:
             return k
     if "copyBuffer" in name:
@@ -260,7 +260,7 @@ def summarize_stats(stats_csv, command, config="cgspn1k", pass_="fwd", name=None
 
 GSPN_KERNELS = ("fused_scan_kernel", "fused_scan_batched_kernel", "fused_bwd_kernel", "adjoint_scan_kernel",
                 "line_scan_kernel", "transpose_kernel", "convert_kernel", "merge_kernel", "merge_dirs_kernel",
-                "direction_kernel")
+                "direction_kernel", "outproj_kernel", "rms_scale_kernel")
 
 
 def summarize_trace(trace_csv, command, config, pass_, warmup, steps, name=None):
@@ -388,7 +388,8 @@ def bench_block(args):
     """The compressed block on the 1K block workload: tokens per second.
 
     One step is one gspn_block_fwd call: the input projection (rocBLAS), the
-    scan (libgspn kernels), the output projection (rocBLAS).  The roofline
+    scan (libgspn kernels), the output projection with the RMS normalisation
+    fused into it (a libgspn MFMA kernel).  The roofline
     counts the bytes no implementation can avoid (x read, z written, both
     weight matrices read once) against HBM; the GEMM rate is reported
     beside it.
@@ -439,7 +440,7 @@ def bench_block(args):
     flops = 2 * B * HW * C * (rows + Cp)
     med = float(np.median(per))
     out = {
-        "metric": "C-GSPN compressed block forward, tokens/s (projection, scan, projection back)",
+        "metric": "C-GSPN compressed block forward, tokens/s (projection, scan, RMS normalisation fused into the projection back)",
         "value": round(B * HW * args.steps / elapsed, 1),
         "unit": "tokens/s",
         "n_gpus": 1,

@@ -110,7 +110,7 @@ enum {
     GSPN_ERR_ALIAS = -8,  /* an output overlaps an input or another output */
     GSPN_ERR_HIP = -9,    /* a HIP call failed; see gspn_last_error() */
     GSPN_ERR_PATH = -10,  /* unknown path, or the path (or the backward) cannot take this shape */
-    GSPN_ERR_FLAGS = -11, /* unknown bit in flags (gspn_scan_fwd_ex, gspn_scan_bwd_ex) */
+    GSPN_ERR_FLAGS = -11, /* unknown bit in flags (gspn_scan_fwd_ex, gspn_scan_bwd_ex, gspn_block_fwd) */
     GSPN_ERR_SCRATCH = -12 /* the shape's workspace exceeds GSPN_NOALLOC_SCRATCH_BYTES (gspn_scan_fwd_noalloc) */
 };
 
@@ -304,18 +304,35 @@ int gspn_scan_bwd_ex(const void *x, const void *w_raw, const void *lam, const vo
                      uint32_t dirs, int32_t groups, int32_t ch_per_weight, uint32_t flags, int32_t dtype,
                      hipStream_t stream);
 
+/* Flags of gspn_block_fwd. */
+enum {
+    GSPN_BLOCK_RMSNORM = 1 /* normalise each pixel's scan output by its RMS over C_proxy before projecting back */
+};
+#define GSPN_BLOCK_NORM_EPS 1e-6f
+
 /*
  * The compressed propagation block around the scan (GSPN-2 author response,
  * "Relate Compressive Proxy Dimension to Low-rank Approximation": x is
  * projected to x_proxy with C_proxy channels by a lightweight linear layer,
  * the recurrence runs there, and the result is projected back to C; C-GSPN
- * abstract: a compressed latent-space propagation block).  Per pixel:
+ * abstract: a compressed latent-space propagation block with fused
+ * normalization).  Per pixel:
  *   [x_proxy; a; lam; u] = w_in x      (a: the raw taps of the scan)
  *   y = gspn_scan_fwd(x_proxy, a, lam, u)   over C_proxy channels
+ *   with GSPN_BLOCK_RMSNORM: y <- y / sqrt(mean over the C_proxy channels
+ *                            of y^2 + GSPN_BLOCK_NORM_EPS)
  *   z = w_out y
  * The pages do not say how the taps, lam and u are generated; here they are
- * further rows of the input projection (plain linear, no activation).  The
- * weight normalisation is the scan's own (fused in its kernels).
+ * further rows of the input projection (plain linear, no activation).  Nor
+ * do they name the block's normalisation: it is read as an RMS
+ * normalisation of the propagated latent, with no learned gain (w_out
+ * absorbs a per-channel gain), fused into the output projection: for bf16
+ * with C_proxy in {16, 32, 64, 128, 256}, C % 32 == 0 and H*W % 8 == 0 one
+ * hand-written MFMA kernel computes the RMS of each pixel from the same
+ * C_proxy values it multiplies (other shapes: a rocBLAS GEMM, then a
+ * scaling pass).  The taps' own sigmoid-then-row normalisation is the
+ * scan's (fused in its kernels).
+ *   flags : 0 or GSPN_BLOCK_RMSNORM; other bits give GSPN_ERR_FLAGS.
  *   x     : [B][C][H][W]
  *   w_in  : [gspn_block_rows(C_proxy, dirs, ch_per_weight)][C], row-major;
  *           rows: x_proxy (C_proxy), the raw taps (one slab of
@@ -330,8 +347,11 @@ int gspn_scan_bwd_ex(const void *x, const void *w_raw, const void *lam, const vo
  * gspn_block_rows).  For H, W <= 64 the fused scan reads g in place
  * (workspace (rows + C_proxy) * B*H*W elements); otherwise g's row blocks
  * are copied into contiguous tensors and the scan is gspn_scan_fwd on the
- * automatic path (workspace (2*rows + C_proxy) * B*H*W elements).  The
- * projections are rocBLAS GEMMs with fp32 accumulation.  The first call on a
+ * automatic path (workspace (2*rows + C_proxy) * B*H*W elements).  When
+ * the normalisation follows a library GEMM (the shapes the MFMA kernel does
+ * not take) the GEMM writes fp32 into B*C*H*W*4 more workspace bytes and
+ * the scaling pass rounds z once.  The input projection is a rocBLAS GEMM;
+ * both projections accumulate in fp32.  The first call on a
  * device creates a rocBLAS handle that the library keeps until the process
  * ends (the scan entry points hold no state); calls are serialised on it by
  * a mutex while they enqueue, and only enqueue work on `stream`.  Sizes, dirs, groups, ch_per_weight
@@ -341,7 +361,7 @@ int gspn_scan_bwd_ex(const void *x, const void *w_raw, const void *lam, const vo
  */
 int gspn_block_fwd(const void *x, const void *w_in, const void *w_out, void *z, int64_t B, int64_t C,
                    int64_t C_proxy, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
-                   int32_t ch_per_weight, int32_t dtype, hipStream_t stream);
+                   int32_t ch_per_weight, uint32_t flags, int32_t dtype, hipStream_t stream);
 
 /* Rows of gspn_block_fwd's w_in, 3*C_proxy + 3*popcount(dirs)*(C_proxy/ch_per_weight),
  * or a negative GSPN_ERR_* code for invalid arguments. */

@@ -276,13 +276,15 @@ def block_rows(C_proxy: int, *, dirs: int = DIR_ALL, ch_per_weight: int = 1) -> 
     return n
 
 
-def block_fwd(x, w_in, w_out, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1, out=None):
+def block_fwd(x, w_in, w_out, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1,
+              norm: bool = True, out=None):
     """The compressed propagation block (gspn_block_fwd) on the current stream.
 
     x: [B, C, H, W]; w_in: [block_rows(C_proxy), C]; w_out: [C, C_proxy];
     returns z: [B, C, H, W] = w_out (scan of the C_proxy-channel projection
     of x, with taps, lambda and u projected from x by the further rows of
-    w_in).
+    w_in), each pixel's scan output divided by its RMS over the C_proxy
+    channels first when norm is set.
     """
     import torch
     for name, t in (("x", x), ("w_in", w_in), ("w_out", w_out)):
@@ -306,7 +308,7 @@ def block_fwd(x, w_in, w_out, *, dirs: int = DIR_ALL, groups: int = 1, ch_per_we
     stream = torch.cuda.current_stream(x.device).cuda_stream
     with torch.cuda.device(x.device):
         rc = _lib.block_fwd_ptr(x.data_ptr(), w_in.data_ptr(), w_out.data_ptr(), out.data_ptr(), B, C, Cp, H, W,
-                                dirs=dirs, groups=groups, ch_per_weight=ch_per_weight, dtype=_dtype_code(x),
-                                stream=stream)
+                                dirs=dirs, groups=groups, ch_per_weight=ch_per_weight,
+                                flags=_lib.BLOCK_RMSNORM if norm else 0, dtype=_dtype_code(x), stream=stream)
     _lib.check(rc)
     return out

@@ -23,6 +23,7 @@ DIR_TB, DIR_BT, DIR_LR, DIR_RL, DIR_ALL = 1, 2, 4, 8, 15
 LAM_PER_DIR, U_PER_DIR = 1, 2
 MAX_BATCH = 32
 NOALLOC_SCRATCH_BYTES = 64 << 20
+BLOCK_RMSNORM = 1
 ERR_SCRATCH = -12
 
 
@@ -80,7 +81,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.gspn_scan_bwd_ex.restype = ctypes.c_int
         lib.gspn_bwd_supported.argtypes = [i64, i64, i64, i64, u32, i32, i32, i32]
         lib.gspn_bwd_supported.restype = ctypes.c_int
-        lib.gspn_block_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, u32, i32, i32, i32, vp]
+        lib.gspn_block_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, u32, i32, i32, u32, i32, vp]
         lib.gspn_block_fwd.restype = ctypes.c_int
         lib.gspn_block_rows.argtypes = [i64, u32, i32]
         lib.gspn_block_rows.restype = ctypes.c_int64
@@ -161,11 +162,11 @@ def select_path(B, C, H, W, *, dirs=DIR_ALL, groups=1, ch_per_weight=1, dtype=GS
 
 
 def block_fwd_ptr(x: int, w_in: int, w_out: int, z: int, B: int, C: int, C_proxy: int, H: int, W: int, *,
-                  dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1, dtype: int = GSPN_BF16,
-                  stream: int = 0) -> int:
+                  dirs: int = DIR_ALL, groups: int = 1, ch_per_weight: int = 1, flags: int = 1,
+                  dtype: int = GSPN_BF16, stream: int = 0) -> int:
     """Raw call of the compressed block on device pointers; returns the status code."""
-    return load().gspn_block_fwd(x, w_in, w_out, z, B, C, C_proxy, H, W, dirs, groups, ch_per_weight, dtype,
-                                 stream)
+    return load().gspn_block_fwd(x, w_in, w_out, z, B, C, C_proxy, H, W, dirs, groups, ch_per_weight, flags,
+                                 dtype, stream)
 
 
 def block_rows(C_proxy: int, dirs: int = DIR_ALL, ch_per_weight: int = 1) -> int:

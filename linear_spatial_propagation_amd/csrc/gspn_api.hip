@@ -395,13 +395,15 @@ int blas_handle(rocblas_handle* h) {
 // For each batch b: Out_b (N x P, row-major, batch stride so) = Wt (N x K,
 // row-major) * In_b (K x P, row-major, batch stride si).  In rocBLAS's
 // column-major terms Out_b^T = In_b^T * Wt^T, with no transposes.
+// out_f32: the output is fp32 whatever the input dtype.
 int gemm_rows(rocblas_handle h, int64_t N, int64_t K, int64_t P, const void* Wt, const void* in, int64_t si,
-              void* out, int64_t so, int64_t batch, bool bf16) {
+              void* out, int64_t so, int64_t batch, bool bf16, bool out_f32 = false) {
     const rocblas_datatype t = bf16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+    const rocblas_datatype to = out_f32 ? rocblas_datatype_f32_r : t;
     const float alpha = 1.0f, beta = 0.0f;
     const rocblas_status st = rocblas_gemm_strided_batched_ex(
         h, rocblas_operation_none, rocblas_operation_none, (rocblas_int)P, (rocblas_int)N, (rocblas_int)K, &alpha,
-        in, t, (rocblas_int)P, si, Wt, t, (rocblas_int)K, 0, &beta, out, t, (rocblas_int)P, so, out, t,
+        in, t, (rocblas_int)P, si, Wt, t, (rocblas_int)K, 0, &beta, out, to, (rocblas_int)P, so, out, to,
         (rocblas_int)P, so, (rocblas_int)batch, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
     if (st != rocblas_status_success) {
         snprintf(g_last_error, sizeof(g_last_error), "rocblas_gemm_strided_batched_ex: %s",
@@ -428,8 +430,10 @@ int64_t gspn_block_rows(int64_t C_proxy, uint32_t dirs, int32_t ch_per_weight) {
 
 int gspn_block_fwd(const void* x, const void* w_in, const void* w_out, void* z, int64_t B, int64_t C,
                    int64_t C_proxy, int64_t H, int64_t W, uint32_t dirs, int32_t groups, int32_t ch_per_weight,
-                   int32_t dtype, hipStream_t stream) {
+                   uint32_t flags, int32_t dtype, hipStream_t stream) {
     g_last_error[0] = '\0';
+    if (flags & ~(uint32_t)GSPN_BLOCK_RMSNORM) return GSPN_ERR_FLAGS;
+    const bool norm = (flags & GSPN_BLOCK_RMSNORM) != 0;
     if (C <= 0 || C > (1LL << 22)) return GSPN_ERR_SHAPE;
     int rc = check_sizes(B, C_proxy, H, W, dirs, groups, ch_per_weight, dtype);
     if (rc) return rc;
@@ -451,13 +455,16 @@ int gspn_block_fwd(const void* x, const void* w_in, const void* w_out, void* z, 
 
     // workspace: g (the input projection, [B][rows][HW]) | y | and, unless
     // the fused scan reads g in place, x_proxy | taps (nd slabs) | lam | u;
-    // each 256-byte aligned
+    // then, when the normalisation follows a library GEMM, that GEMM's fp32
+    // output (rounded once, by the scaling pass); each 256-byte aligned
     const bool in_place = auto_path(H, W) == GSPN_PATH_FUSED;
+    const bool mfma_out = gspn::outproj_supported((int)Cp, (int)C, (int)HW, bf16);
     auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
     const size_t ep = (size_t)B * Cp * HW * es, et = (size_t)nd * B * Cw * 3 * HW * es;
     const size_t o_g = 0, o_y = al((size_t)B * rows * HW * es), o_x = o_y + al(ep), o_t = o_x + al(ep),
                  o_l = o_t + al(et), o_u = o_l + al(ep);
-    const size_t total = in_place ? o_x : o_u + al(ep);
+    const size_t o_zf = in_place ? o_x : o_u + al(ep);
+    const size_t total = o_zf + (norm && !mfma_out ? al((size_t)B * C * HW * sizeof(float)) : 0);
     char* work = nullptr;
     hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&work), total, stream);
     if (e != hipSuccess) { set_error("hipMallocAsync(workspace)", e); return GSPN_ERR_HIP; }
@@ -511,8 +518,28 @@ int gspn_block_fwd(const void* x, const void* w_in, const void* w_out, void* z, 
         if (rc == GSPN_OK && !in_place)
             rc = scan_fwd_impl(work + o_x, work + o_t, work + o_l, work + o_u, work + o_y, B, Cp, H, W, dirs,
                                groups, ch_per_weight, 0u, dtype, GSPN_PATH_AUTO, stream);
-        // z: [B][C][HW] = w_out (C x C_proxy) * y_b
-        if (rc == GSPN_OK) rc = gemm_rows(h, C, Cp, HW, w_out, work + o_y, Cp * HW, z, C * HW, B, bf16);
+        // z: [B][C][HW] = w_out (C x C_proxy) * y_b, each pixel scaled by the
+        // 1 / rms of its C_proxy scan outputs when normalising: one
+        // hand-written MFMA kernel when the shape allows, else the library
+        // GEMM followed by the scaling
+        if (rc == GSPN_OK) {
+            if (mfma_out) {
+                const hipError_t el = gspn::launch_outproj(work + o_y, w_out, z, (int)B, (int)Cp, (int)C, (int)HW,
+                                                           norm, GSPN_BLOCK_NORM_EPS, stream);
+                if (el != hipSuccess) { set_error("output projection launch", el); rc = GSPN_ERR_HIP; }
+            } else if (!norm) {
+                rc = gemm_rows(h, C, Cp, HW, w_out, work + o_y, Cp * HW, z, C * HW, B, bf16);
+            } else {
+                // fp32 GEMM output, scaled and rounded to the dtype once
+                rc = gemm_rows(h, C, Cp, HW, w_out, work + o_y, Cp * HW, work + o_zf, C * HW, B, bf16, true);
+                if (rc == GSPN_OK) {
+                    const hipError_t el = gspn::launch_rms_scale(work + o_y, reinterpret_cast<const float*>(work + o_zf), z,
+                                                                 (int)B, (int)Cp, (int)C,
+                                                                 (int)HW, bf16, GSPN_BLOCK_NORM_EPS, stream);
+                    if (el != hipSuccess) { set_error("normalisation launch", el); rc = GSPN_ERR_HIP; }
+                }
+            }
+        }
     }
     const hipError_t ef = hipFreeAsync(work, stream);
     if (rc != GSPN_OK) return rc;

@@ -68,6 +68,16 @@ hipError_t launch_fused_bwd(const GradArgs& g, hipStream_t stream);
 size_t lines_bwd_workspace_bytes(const GradArgs& g);
 hipError_t launch_lines_bwd(const GradArgs& g, void* workspace, hipStream_t stream);
 
+// Compressed block: the output projection with the block's RMS
+// normalisation fused (bf16; C_proxy in {16, 32, 64, 128, 256}, C % 32 == 0,
+// H*W % 8 == 0), and the normalisation alone for the other shapes: it
+// scales the fp32 z a library GEMM computed and rounds it into the output.
+bool outproj_supported(int Cp, int C, int HW, bool bf16);
+hipError_t launch_outproj(const void* y, const void* w_out, void* z, int B, int Cp, int C, int HW, bool norm,
+                          float eps, hipStream_t stream);
+hipError_t launch_rms_scale(const void* y, const float* zf, void* z, int B, int Cp, int C, int HW, bool bf16,
+                            float eps, hipStream_t stream);
+
 // Per-line fallback: any H, W <= 4096.  `planes` is an fp32 workspace of
 // popcount(dirs) * B*C*H*W floats.
 hipError_t launch_general(const ScanArgs& a, float* planes, hipStream_t stream);

@@ -199,15 +199,23 @@ def block_rows(C_proxy: int, dirs: int, cpw: int) -> int:
     return C_proxy + nd * (C_proxy // cpw) * 3 + 2 * C_proxy
 
 
-def block_fwd(x, w_in, w_out, *, dirs: int = 15, groups: int = 1, cpw: int = 1, io_round=None,
-              nthreads: int = 0, lib=None) -> np.ndarray:
+BLOCK_NORM_EPS = 1e-6
+
+
+def block_fwd(x, w_in, w_out, *, dirs: int = 15, groups: int = 1, cpw: int = 1, norm: bool = True,
+              io_round=None, nthreads: int = 0, lib=None) -> np.ndarray:
     """The compressed propagation block around the scan, in fp64.
 
     Reading of the block (GSPN-2 response, *Relate Compressive Proxy
     Dimension to Low-rank Approximation*; C-GSPN abstract): per pixel, one
     linear layer maps the C input channels to x_proxy (C_proxy channels),
     the raw taps, lambda and u; the scan runs over x_proxy; a second linear
-    layer maps its C_proxy output channels back to C.
+    layer maps its C_proxy output channels back to C.  With norm (the
+    block's "fused normalization", C-GSPN abstract, read as an RMS
+    normalisation in the compressed space): before the output projection the
+    scan output of each pixel is divided by its root mean square over the
+    C_proxy channels, sqrt(mean_c y_c^2 + BLOCK_NORM_EPS); no learned gain
+    (a per-channel gain is a diagonal factor that w_out absorbs).
 
     x: [B][C][H][W]; w_in: [block_rows][C], rows in the order x_proxy
     (C_proxy), the raw taps (one slab per enabled direction, TB, BT, LR, RL;
@@ -235,7 +243,10 @@ def block_fwd(x, w_in, w_out, *, dirs: int = 15, groups: int = 1, cpw: int = 1, 
     lam = rnd(g[:, t1:t1 + Cp]).reshape(B, Cp, H, W)
     u = rnd(g[:, t1 + Cp:]).reshape(B, Cp, H, W)
     y = rnd(scan_fwd(xp, taps, lam, u, dirs=dirs, groups=groups, cpw=cpw, nthreads=nthreads, lib=lib))
-    return np.matmul(w_out, y.reshape(B, Cp, H * W)).reshape(B, C, H, W)
+    y = y.reshape(B, Cp, H * W)
+    if norm:
+        y = y / np.sqrt(np.mean(y * y, axis=1, keepdims=True) + BLOCK_NORM_EPS)
+    return np.matmul(w_out, y).reshape(B, C, H, W)
 
 def slice_fwd(x, w, lam, u, *, dirs: int = 15, groups: int = 1) -> np.ndarray:
     """One slice: x, lam, u [H][W]; w [popcount(dirs)][3][H][W] -> y [H][W]."""

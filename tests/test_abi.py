@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_strings(lib):
     assert lib.gspn_version() == 1
-    for code in range(0, -11, -1):
+    for code in range(0, -13, -1):
         s = _lib.status_string(code)
         assert s.startswith("GSPN_"), (code, s)
     assert "unknown" in _lib.status_string(-99)
@@ -225,18 +225,18 @@ def test_variant_bwd_flags_zero_is_the_shared_backward(lib):
 
 def call_block(**kw):
     args = dict(x=FAKE, w_in=FAKE + (1 << 32), w_out=FAKE + (2 << 32), z=FAKE + (3 << 32), B=2, C=24, C_proxy=8,
-                H=16, W=16, dirs=15, groups=1, ch_per_weight=2, dtype=1)
+                H=16, W=16, dirs=15, groups=1, ch_per_weight=2, flags=1, dtype=1)
     args.update(kw)
     return _lib.block_fwd_ptr(args["x"], args["w_in"], args["w_out"], args["z"], args["B"], args["C"],
                               args["C_proxy"], args["H"], args["W"], dirs=args["dirs"], groups=args["groups"],
-                              ch_per_weight=args["ch_per_weight"], dtype=args["dtype"])
+                              ch_per_weight=args["ch_per_weight"], flags=args["flags"], dtype=args["dtype"])
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), -2), (dict(C=0), -2), (dict(C_proxy=0), -2), (dict(W=4097), -2), (dict(B=1 << 20, C=1 << 10), -2),
     (dict(dirs=0), -3), (dict(dirs=16), -3), (dict(groups=3), -4), (dict(ch_per_weight=3), -5),
     (dict(dtype=2), -6), (dict(x=0), -1), (dict(w_in=0), -1), (dict(w_out=0), -1), (dict(z=0), -1),
-    (dict(z=FAKE + (3 << 32) + 8), -7),
+    (dict(z=FAKE + (3 << 32) + 8), -7), (dict(flags=2), -11), (dict(flags=0x80000001), -11),
     (dict(z=FAKE), -8),                              # z on x
     (dict(z=FAKE + (1 << 32) + 1024), -8),           # z inside w_in
     (dict(z=FAKE + (2 << 32) - 256), -8),            # z runs into w_out

@@ -27,9 +27,11 @@ def keep_f32(a):
     return np.asarray(a, dtype=np.float32).astype(np.float64)
 
 
-def stand_in(inp, x, w_in, w_out, r_g, r_y, r_z):
+def stand_in(inp, x, w_in, w_out, r_g, r_y, r_z, norm=True):
     """Block with fp32 GEMMs; r_g rounds the generated tensors, r_y the scan
-    output, r_z the block output."""
+    output, r_z the block output.  norm: the RMS normalisation of each
+    pixel's scan output over the proxy channels, in fp32, applied to the
+    projection's fp32 sums.  Returns z and the normalised scan output."""
     B, C, H, W = x.shape
     Cp, nd, Cw = inp.C_proxy, bin(inp.dirs).count("1"), inp.C_proxy // inp.cpw
     g = np.matmul(w_in.astype(np.float32), x.reshape(B, C, H * W).astype(np.float32)).astype(np.float64)
@@ -39,8 +41,13 @@ def stand_in(inp, x, w_in, w_out, r_g, r_y, r_z):
     lam = r_g(g[:, t1:t1 + Cp]).reshape(B, Cp, H, W)
     u = r_g(g[:, t1 + Cp:]).reshape(B, Cp, H, W)
     y = r_y(oracle.scan_fwd(xp, taps, lam, u, dirs=inp.dirs, groups=inp.groups, cpw=inp.cpw))
-    z = np.matmul(w_out.astype(np.float32), y.reshape(B, Cp, H * W).astype(np.float32)).astype(np.float64)
-    return r_z(z).reshape(B, w_out.shape[0], H, W), y
+    y32 = y.reshape(B, Cp, H * W).astype(np.float32)
+    inv = np.ones((B, 1, H * W), np.float32)
+    if norm:
+        inv = np.float32(1.0) / np.sqrt(np.mean(y32 * y32, axis=1, keepdims=True) + np.float32(oracle.BLOCK_NORM_EPS))
+    z = (np.matmul(w_out.astype(np.float32), y32) * inv).astype(np.float64)
+    y_n = (y32 * inv).astype(np.float64).reshape(B, Cp, H, W)
+    return r_z(z).reshape(B, w_out.shape[0], H, W), y_n
 
 
 SHAPES = [

@@ -28,23 +28,23 @@ from linear_spatial_propagation_amd.inputs import BLOCK_CONFIGS, BlockInputs
 
 pytestmark = pytest.mark.gpu
 
-def run_block(inp, out_batches=None):
+def run_block(inp, out_batches=None, norm=True):
     import torch
     import linear_spatial_propagation_amd as gspn
     x, wi, wo = (to_device(a, inp.dtype) for a in (inp.x_store, inp.w_in_store, inp.w_out_store))
-    z = gspn.block_fwd(x, wi, wo, dirs=inp.dirs, groups=inp.groups, ch_per_weight=inp.cpw)
+    z = gspn.block_fwd(x, wi, wo, dirs=inp.dirs, groups=inp.groups, ch_per_weight=inp.cpw, norm=norm)
     torch.cuda.synchronize()
     if out_batches is not None:
         z = z[out_batches]
     return from_device(z.contiguous(), inp.dtype)
 
 
-def oracle_block(inp, batches=None):
+def oracle_block(inp, batches=None, norm=True):
     x, wi, wo = inp.f64()
     if batches is not None:
         x = x[batches]
     rnd = oracle.round_bf16 if inp.dtype == "bf16" else None
-    z = oracle.block_fwd(x, wi, wo, dirs=inp.dirs, groups=inp.groups, cpw=inp.cpw, io_round=rnd)
+    z = oracle.block_fwd(x, wi, wo, dirs=inp.dirs, groups=inp.groups, cpw=inp.cpw, norm=norm, io_round=rnd)
     return z, wo
 
 
@@ -58,36 +58,46 @@ CASES = [
     (2, 64, 32, 16, 16, 15, 1, 4),
     (1, 96, 64, 24, 40, 15, 1, 8),
     (2, 160, 128, 8, 16, 15, 2, 16),  # the proxy width of the 1K block
+    # the hand-written output projection (bf16): C_proxy in {16, ..., 256},
+    # C % 32 == 0, H*W % 8 == 0, a partial last tile of 128 pixels
+    (1, 32, 16, 9, 8, 15, 1, 4),
+    (2, 64, 256, 12, 20, 15, 1, 32),
+    (1, 96, 64, 17, 24, 3, 1, 8),
 ]
 
 
+@pytest.mark.parametrize("norm", [True, False], ids=["rmsnorm", "plain"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
-def test_block_parity(case, dtype):
+def test_block_parity(case, dtype, norm):
     B, C, Cp, H, W, dirs, groups, cpw = case
     inp = BlockInputs(B, C, Cp, H, W, rows=oracle.block_rows(Cp, dirs, cpw), dirs=dirs, groups=groups,
                       cpw=cpw, dtype=dtype, seed=sum(case))
-    say(f"block {case} {dtype}")
-    z = run_block(inp)
-    zhat, wo = oracle_block(inp)
+    say(f"block {case} {dtype} norm={norm}")
+    z = run_block(inp, norm=norm)
+    zhat, wo = oracle_block(inp, norm=norm)
     rnd = oracle.round_bf16 if dtype == "bf16" else None
     x, wi, _ = inp.f64()
-    y = _scan_out(inp, x, wi, rnd)
+    y = _scan_out(inp, x, wi, rnd, norm)
     err = block_error(z, zhat, wo, np.abs(y), dtype)
     say(f"  pointwise {err['pointwise']:.3e} l2 {err['l2']:.3e} (tol {BLOCK_TOL[dtype]})")
     assert block_passes(err, dtype), err
 
 
-def _scan_out(inp, x, wi, rnd):
-    """The scan output inside the oracle's block (for the metric's scale)."""
+def _scan_out(inp, x, wi, rnd, norm=True):
+    """The (normalised) scan output inside the oracle's block, the operand of
+    the output projection (for the metric's scale)."""
     B, C, H, W = x.shape
     Cp, nd, Cw = inp.C_proxy, bin(inp.dirs).count("1"), inp.C_proxy // inp.cpw
     r = rnd or (lambda a: a)
     g = np.matmul(wi, x.reshape(B, C, H * W))
     t0, t1 = Cp, Cp + nd * Cw * 3
     taps = r(g[:, t0:t1]).reshape(B, nd, Cw, 3, H, W).transpose(1, 0, 2, 3, 4, 5)
-    return oracle.scan_fwd(r(g[:, :Cp]).reshape(B, Cp, H, W), taps, r(g[:, t1:t1 + Cp]).reshape(B, Cp, H, W),
-                           r(g[:, t1 + Cp:]).reshape(B, Cp, H, W), dirs=inp.dirs, groups=inp.groups, cpw=inp.cpw)
+    y = r(oracle.scan_fwd(r(g[:, :Cp]).reshape(B, Cp, H, W), taps, r(g[:, t1:t1 + Cp]).reshape(B, Cp, H, W),
+                          r(g[:, t1 + Cp:]).reshape(B, Cp, H, W), dirs=inp.dirs, groups=inp.groups, cpw=inp.cpw))
+    if norm:
+        y = y / np.sqrt(np.mean(y * y, axis=1, keepdims=True) + oracle.BLOCK_NORM_EPS)
+    return y
 
 
 def test_block1k_sampled_batches():

@@ -14,6 +14,8 @@ and u; the scan over x_proxy; a per-pixel linear layer back to C channels.
   oracle on those constants.
 - round_bf16 is pinned on hand-picked ties and on torch's own conversion.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -21,10 +23,12 @@ import oracle
 from bruteforce import bruteforce_fwd
 
 
-def _block_loops(x, w_in, w_out, dirs, groups, cpw, rnd=None):
+def _block_loops(x, w_in, w_out, dirs, groups, cpw, rnd=None, norm=False):
     """The block by pixel loops; rnd (if given) rounds each generated value
     and each scan output one at a time, the places a block that stores its
-    intermediates in a narrower dtype rounds them."""
+    intermediates in a narrower dtype rounds them.  norm: each pixel's scan
+    output is divided by its root mean square over the proxy channels
+    (sqrt(sum_q y_q^2 / C_proxy + eps)) before the output projection."""
     rnd = rnd or (lambda v: v)
     B, C, H, W = x.shape
     Cp = w_out.shape[1]
@@ -51,6 +55,13 @@ def _block_loops(x, w_in, w_out, dirs, groups, cpw, rnd=None):
     u = g[:, base + Cp:base + 2 * Cp]
     y = bruteforce_fwd(xp, taps, lam, u, dirs=dirs, groups=groups, cpw=cpw)
     y = np.vectorize(rnd)(y)
+    if norm:
+        for b in range(B):
+            for i in range(H):
+                for j in range(W):
+                    ms = sum(y[b, q, i, j] ** 2 for q in range(Cp)) / Cp
+                    for q in range(Cp):
+                        y[b, q, i, j] /= math.sqrt(ms + oracle.BLOCK_NORM_EPS)
     z = np.zeros((B, C, H, W))
     for b in range(B):
         for c in range(C):
@@ -66,14 +77,15 @@ def _block_loops(x, w_in, w_out, dirs, groups, cpw, rnd=None):
     (1, 5, 2, 4, 4, 6, 2, 2),     # BT and LR only, groups of two lines
     (1, 2, 3, 2, 5, 9, 1, 3),     # TB and RL, one weight set for three channels
 ])
-def test_block_matches_pixel_loops_and_dense_scan(case):
+@pytest.mark.parametrize("norm", [False, True])
+def test_block_matches_pixel_loops_and_dense_scan(case, norm):
     B, C, Cp, H, W, dirs, groups, cpw = case
     rng = np.random.default_rng(sum(case))
     x = rng.standard_normal((B, C, H, W))
     w_in = rng.standard_normal((oracle.block_rows(Cp, dirs, cpw), C)) * 0.7
     w_out = rng.standard_normal((C, Cp))
-    z = oracle.block_fwd(x, w_in, w_out, dirs=dirs, groups=groups, cpw=cpw)
-    ref = _block_loops(x, w_in, w_out, dirs, groups, cpw)
+    z = oracle.block_fwd(x, w_in, w_out, dirs=dirs, groups=groups, cpw=cpw, norm=norm)
+    ref = _block_loops(x, w_in, w_out, dirs, groups, cpw, norm=norm)
     np.testing.assert_allclose(z, ref, rtol=1e-11, atol=1e-12)
 
 
@@ -85,15 +97,15 @@ def test_block_row_blocks_are_distinguished():
     x = rng.standard_normal((B, C, H, W))
     w_in = rng.standard_normal((oracle.block_rows(Cp, dirs, cpw), C))
     w_out = rng.standard_normal((C, Cp))
-    z = oracle.block_fwd(x, w_in, w_out, dirs=dirs, cpw=cpw)
+    z = oracle.block_fwd(x, w_in, w_out, dirs=dirs, cpw=cpw, norm=False)
     nd, Cw = 4, Cp // cpw
     base = Cp + nd * Cw * 3
     swapped = w_in.copy()
     swapped[base:base + Cp], swapped[base + Cp:] = w_in[base + Cp:], w_in[base:base + Cp]
-    assert np.abs(oracle.block_fwd(x, swapped, w_out, dirs=dirs, cpw=cpw) - z).max() > 1e-3
+    assert np.abs(oracle.block_fwd(x, swapped, w_out, dirs=dirs, cpw=cpw, norm=False) - z).max() > 1e-3
     slabs = w_in.copy()
     slabs[Cp:Cp + 6], slabs[Cp + 6:Cp + 12] = w_in[Cp + 6:Cp + 12], w_in[Cp:Cp + 6]
-    assert np.abs(oracle.block_fwd(x, slabs, w_out, dirs=dirs, cpw=cpw) - z).max() > 1e-3
+    assert np.abs(oracle.block_fwd(x, slabs, w_out, dirs=dirs, cpw=cpw, norm=False) - z).max() > 1e-3
 
 
 def test_block_with_constant_generated_tensors_is_the_projected_scan():
@@ -117,7 +129,7 @@ def test_block_with_constant_generated_tensors_is_the_projected_scan():
     w_in[base:base + Cp, C - 1] = lam_vals
     w_in[base + Cp:, C - 1] = u_vals
     w_out = rng.standard_normal((C, Cp))
-    z = oracle.block_fwd(x, w_in, w_out, dirs=dirs, groups=groups, cpw=cpw)
+    z = oracle.block_fwd(x, w_in, w_out, dirs=dirs, groups=groups, cpw=cpw, norm=False)
     taps = np.broadcast_to(tap_vals[:, None, :, :, None, None], (nd, B, Cw, 3, H, W))
     lam = np.broadcast_to(lam_vals[None, :, None, None], (B, Cp, H, W))
     u = np.broadcast_to(u_vals[None, :, None, None], (B, Cp, H, W))
@@ -160,10 +172,42 @@ def test_block_io_rounding_placement(case):
     w_in = rng.standard_normal((oracle.block_rows(Cp, dirs, cpw), C)) * 0.7
     w_out = rng.standard_normal((C, Cp))
     z = oracle.block_fwd(x, w_in, w_out, dirs=dirs, groups=groups, cpw=cpw, io_round=oracle.round_bf16)
-    ref = _block_loops(x, w_in, w_out, dirs, groups, cpw, rnd=_bf16_scalar)
+    ref = _block_loops(x, w_in, w_out, dirs, groups, cpw, rnd=_bf16_scalar, norm=True)
     np.testing.assert_allclose(z, ref, rtol=1e-11, atol=1e-12)
     # the rounding is really applied, at both places
     exact = oracle.block_fwd(x, w_in, w_out, dirs=dirs, groups=groups, cpw=cpw)
     assert np.abs(z - exact).max() > 1e-4
-    gen_only = _block_loops(x, w_in, w_out, dirs, groups, cpw, rnd=None)
+    gen_only = _block_loops(x, w_in, w_out, dirs, groups, cpw, rnd=None, norm=True)
     assert np.abs(gen_only - ref).max() > 1e-4
+
+
+def test_block_norm_removes_the_scale_of_the_proxy():
+    # y is linear in x_proxy, so scaling the x_proxy rows of w_in by a > 0
+    # scales y by a: with the normalisation z is unchanged (the eps term
+    # aside), without it z scales by a
+    B, C, Cp, H, W, dirs, cpw = 2, 5, 4, 5, 6, 15, 2
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((B, C, H, W))
+    w_in = rng.standard_normal((oracle.block_rows(Cp, dirs, cpw), C))
+    w_out = rng.standard_normal((C, Cp))
+    scaled = w_in.copy()
+    scaled[:Cp] *= 7.0
+    z = oracle.block_fwd(x, w_in, w_out, dirs=dirs, cpw=cpw)
+    np.testing.assert_allclose(oracle.block_fwd(x, scaled, w_out, dirs=dirs, cpw=cpw), z, rtol=1e-6, atol=1e-9)
+    zr = oracle.block_fwd(x, w_in, w_out, dirs=dirs, cpw=cpw, norm=False)
+    np.testing.assert_allclose(oracle.block_fwd(x, scaled, w_out, dirs=dirs, cpw=cpw, norm=False), 7.0 * zr,
+                               rtol=1e-11, atol=1e-12)
+
+
+def test_block_norm_gives_unit_mean_square_through_identity():
+    # with w_out the identity (C = C_proxy) the output of each pixel is the
+    # normalised scan output: its mean square over channels is ms / (ms + eps)
+    B, Cp, H, W, dirs, cpw = 1, 6, 4, 5, 15, 3
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((B, Cp, H, W))
+    w_in = rng.standard_normal((oracle.block_rows(Cp, dirs, cpw), Cp))
+    z = oracle.block_fwd(x, w_in, np.eye(Cp), dirs=dirs, cpw=cpw)
+    y = oracle.block_fwd(x, w_in, np.eye(Cp), dirs=dirs, cpw=cpw, norm=False)
+    ms = np.mean(y * y, axis=1)
+    np.testing.assert_allclose(np.mean(z * z, axis=1), ms / (ms + oracle.BLOCK_NORM_EPS), rtol=1e-12)
+    np.testing.assert_allclose(z * np.sqrt(ms + oracle.BLOCK_NORM_EPS)[:, None], y, rtol=1e-12, atol=1e-14)
