@@ -731,7 +731,7 @@ def main():
             "path": ("backward line kernels, per-direction lambda and u" if bwd_variant else
                      "fused backward" if max(H, W) <= 64 else "backward line kernels") if bwd else
                     "line kernels, per-direction lambda and u" if dirs_variant else
-                    {1: "fused", 2: "general"}[gspn.select_path(B, C, H, W, groups=wl.groups,
+                    {1: "fused", 2: "general", 3: "slice"}[gspn.select_path(B, C, H, W, groups=wl.groups,
                                                                 ch_per_weight=wl.cpw)],
             "algorithmic_bytes_per_step": nbytes,
             "buffer_sets": R,

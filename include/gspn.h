@@ -59,7 +59,8 @@
  * base pointers must be 16-byte aligned; y must not overlap any input.  Calls
  * only enqueue work on `stream` and never synchronise; a kernel fault shows
  * at the caller's next synchronisation.  Shapes with H <= 64 and W <= 64 run
- * one fused kernel and allocate nothing.  Larger shapes run the general path
+ * one fused kernel and allocate nothing; so do the local-group shapes of
+ * GSPN_PATH_SLICE (below).  Other shapes run the general path
  * and take a workspace stream-ordered (hipMallocAsync / hipFreeAsync on
  * `stream`): with H, W <= 512 and both multiples of K (1, 2, 4 or 8 as
  * max(H, W) is <= 64, 128, 256 or 512) the line kernels use
@@ -127,7 +128,11 @@ enum {
 enum {
     GSPN_PATH_AUTO = 0,    /* what gspn_scan_fwd uses */
     GSPN_PATH_FUSED = 1,   /* one fused 4-direction kernel; needs H <= 64 and W <= 64 */
-    GSPN_PATH_GENERAL = 2  /* line (or per-line) kernels + merge; any shape; uses a workspace */
+    GSPN_PATH_GENERAL = 2, /* line (or per-line) kernels + merge; any shape; uses a workspace */
+    GSPN_PATH_SLICE = 3    /* one workgroup per (b, c) slice, the sum of the directions held on chip; bf16,
+                              H, W <= 128, W % 8 == 0, H even, groups >= 8, (W / groups) % 8 == 0 when LR or
+                              RL is enabled; no workspace.  GSPN_PATH_AUTO takes it for such shapes when
+                              they do not fit the fused kernel. */
 };
 
 /*
@@ -225,8 +230,9 @@ typedef struct {
 
 int gspn_scan_fwd_batched(const gspn_problem *problems, int32_t count, int32_t dtype, hipStream_t stream);
 
-/* The path gspn_scan_fwd would take for these sizes (GSPN_PATH_FUSED or
- * GSPN_PATH_GENERAL), or a negative error code for invalid sizes. */
+/* The path gspn_scan_fwd would take for these sizes (GSPN_PATH_FUSED,
+ * GSPN_PATH_SLICE or GSPN_PATH_GENERAL), or a negative error code for
+ * invalid sizes. */
 int gspn_select_path(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
                      int32_t ch_per_weight, int32_t dtype);
 

@@ -19,12 +19,12 @@ Tensors (same dtype, float32 or bfloat16, contiguous, on one GPU):
 from __future__ import annotations
 
 from . import _lib
-from ._lib import (DIR_ALL, DIR_BT, DIR_LR, DIR_RL, DIR_TB, PATH_AUTO, PATH_FUSED, PATH_GENERAL,
+from ._lib import (DIR_ALL, DIR_BT, DIR_LR, DIR_RL, DIR_TB, PATH_AUTO, PATH_FUSED, PATH_GENERAL, PATH_SLICE,
                    GspnError, load, select_path)
 
 __all__ = ["scan_fwd", "scan_bwd", "scan_fwd_dirs", "scan_bwd_dirs", "scan_fwd_batched", "gspn_scan", "block_fwd",
            "block_rows", "select_path", "load", "GspnError", "DIR_TB", "DIR_BT", "DIR_LR", "DIR_RL",
-           "DIR_ALL", "PATH_AUTO", "PATH_FUSED", "PATH_GENERAL"]
+           "DIR_ALL", "PATH_AUTO", "PATH_FUSED", "PATH_GENERAL", "PATH_SLICE"]
 
 
 def _dtype_code(t):

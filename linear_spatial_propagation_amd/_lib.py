@@ -18,6 +18,7 @@ GSPN_BF16 = 1
 PATH_AUTO = 0
 PATH_FUSED = 1
 PATH_GENERAL = 2
+PATH_SLICE = 3
 DIR_TB, DIR_BT, DIR_LR, DIR_RL, DIR_ALL = 1, 2, 4, 8, 15
 
 LAM_PER_DIR, U_PER_DIR = 1, 2

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgspn.so")
 SOURCES = ["gspn_api.hip", "gspn_fused.hip", "gspn_lines.hip", "gspn_lines_bwd.hip", "gspn_fused_bwd.hip",
-           "gspn_general.hip", "gspn_block.hip"]
+           "gspn_general.hip", "gspn_block.hip", "gspn_slice.hip"]
 ARCH = "gfx950"
 
 

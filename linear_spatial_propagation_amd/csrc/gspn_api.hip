@@ -81,7 +81,15 @@ const char* gspn_status_string(int status) {
 int gspn_select_path(int64_t B, int64_t C, int64_t H, int64_t W, uint32_t dirs, int32_t groups,
                      int32_t ch_per_weight, int32_t dtype) {
     const int rc = check_sizes(B, C, H, W, dirs, groups, ch_per_weight, dtype);
-    return rc ? rc : auto_path(H, W);
+    if (rc) return rc;
+    const int path = auto_path(H, W);
+    if (path == GSPN_PATH_GENERAL) {
+        gspn::ScanArgs a{};
+        a.B = (int)B; a.C = (int)C; a.H = (int)H; a.W = (int)W;
+        a.dirs = dirs; a.groups = groups; a.cpw = ch_per_weight; a.bf16 = dtype == GSPN_BF16;
+        if (gspn::slice_supported(a)) return GSPN_PATH_SLICE;
+    }
+    return path;
 }
 
 }  // extern "C"
@@ -173,15 +181,6 @@ int scan_fwd_impl(const void* x, const void* w_raw, const void* lam, const void*
     if (overlaps(y, nbytes, x, nbytes) || overlaps(y, nbytes, lam, lbytes) ||
         overlaps(y, nbytes, u, ubytes) || overlaps(y, nbytes, w_raw, wbytes))
         return GSPN_ERR_ALIAS;
-    // per-direction lambda / u run on the line kernels only
-    if (path == GSPN_PATH_AUTO) path = flags ? GSPN_PATH_GENERAL : auto_path(H, W);
-    if (path != GSPN_PATH_FUSED && path != GSPN_PATH_GENERAL) return GSPN_ERR_PATH;
-    if (path == GSPN_PATH_FUSED && (auto_path(H, W) != GSPN_PATH_FUSED || flags)) return GSPN_ERR_PATH;
-    if (flags && !gspn::lines_supported((int)H, (int)W)) {
-        set_error_text("per-direction lambda / u run on the line kernels: H, W <= 512 and multiples of K");
-        return GSPN_ERR_PATH;
-    }
-
     gspn::ScanArgs a;
     a.x = x; a.w = w_raw; a.lam = lam; a.u = u; a.y = y;
     a.B = (int)B; a.C = (int)C; a.H = (int)H; a.W = (int)W;
@@ -189,6 +188,24 @@ int scan_fwd_impl(const void* x, const void* w_raw, const void* lam, const void*
     a.lam_dir = (flags & GSPN_LAM_PER_DIR) != 0;
     a.u_dir = (flags & GSPN_U_PER_DIR) != 0;
 
+    // per-direction lambda / u run on the line kernels only
+    if (path == GSPN_PATH_AUTO) {
+        path = flags ? GSPN_PATH_GENERAL : auto_path(H, W);
+        if (path == GSPN_PATH_GENERAL && gspn::slice_supported(a)) path = GSPN_PATH_SLICE;
+    }
+    if (path != GSPN_PATH_FUSED && path != GSPN_PATH_GENERAL && path != GSPN_PATH_SLICE) return GSPN_ERR_PATH;
+    if (path == GSPN_PATH_FUSED && (auto_path(H, W) != GSPN_PATH_FUSED || flags)) return GSPN_ERR_PATH;
+    if (path == GSPN_PATH_SLICE && !gspn::slice_supported(a)) return GSPN_ERR_PATH;
+    if (flags && !gspn::lines_supported((int)H, (int)W)) {
+        set_error_text("per-direction lambda / u run on the line kernels: H, W <= 512 and multiples of K");
+        return GSPN_ERR_PATH;
+    }
+
+    if (path == GSPN_PATH_SLICE) {
+        const hipError_t e = gspn::launch_slice(a, stream);
+        if (e != hipSuccess) { set_error("slice kernel launch", e); return GSPN_ERR_HIP; }
+        return GSPN_OK;
+    }
     if (path == GSPN_PATH_FUSED) {
         const hipError_t e = gspn::launch_fused(a, stream);
         if (e != hipSuccess) { set_error("fused kernel launch", e); return GSPN_ERR_HIP; }

@@ -78,6 +78,12 @@ hipError_t launch_outproj(const void* y, const void* w_out, void* z, int B, int 
 hipError_t launch_rms_scale(const void* y, const float* zf, void* z, int B, int Cp, int C, int HW, bool bf16,
                             float eps, hipStream_t stream);
 
+// One workgroup per (b, c) slice with the slice's sum in LDS: bf16, shared
+// lambda and u, H, W <= 128, W % 8 == 0, H even, groups >= 8 and, with LR or
+// RL enabled, (W / groups) % 8 == 0.  No workspace.
+bool slice_supported(const ScanArgs& a);
+hipError_t launch_slice(const ScanArgs& a, hipStream_t stream);
+
 // Per-line fallback: any H, W <= 4096.  `planes` is an fp32 workspace of
 // popcount(dirs) * B*C*H*W floats.
 hipError_t launch_general(const ScanArgs& a, float* planes, hipStream_t stream);

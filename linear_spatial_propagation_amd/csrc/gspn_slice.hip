@@ -1,0 +1,421 @@
+// gspn_slice.hip -- the four-direction GSPN scan with one workgroup per
+// (b, c) slice, for local-group grids with sides up to 128 (bf16).
+//
+// Same operator as the other kernels: the line recurrence of "Parallel
+// Sequence Modeling via Generalized Spatial Propagation Network" (CVPR 2025
+// paper notes, "Key design 1"), tridiagonal row-stochastic weights ("Key
+// design 2"), four scan directions merged as y = u * sum_dir h_dir, and the
+// local variant ("Key design 3": each direction's scan axis split into g
+// groups that restart the state).
+//
+// Design (gfx950, wave64), for H, W <= 128 and at least 8 groups:
+//  * One workgroup of 8 waves owns a whole (b, c) slice.  The sum of the
+//    four directions is held in LDS as fp32 (H x 129 floats), so no
+//    per-direction plane goes through HBM and there is no separate merge
+//    pass: every input is read once and y is written once.
+//  * The directions run one after the other (TB, BT, LR, RL: the fixed
+//    summation order); within a direction, wave w scans groups w, w + 8, ...
+//    Lane l owns positions 2l and 2l + 1 of a line, the state is two VGPRs
+//    and the neighbours across lanes come from DPP wave shifts.  The first
+//    enabled direction stores into the LDS sum, the others add; a barrier
+//    separates the directions.
+//  * Row directions read each line (a row) as 4-byte pieces per lane,
+//    loaded four lines ahead.  Column directions read, for each of the
+//    lane's two rows, the group's columns as 16-byte pieces of 8 columns:
+//    the eight waves own the groups side by side, so between them they read
+//    whole 128-byte lines at the same time, with no transposed copy.  Two
+//    pieces are in flight ahead of the scan.
+//  * Taps are normalised as they are consumed (3 exp + 1 rcp per pixel and
+//    direction, the rational form; rows with a tap below -40 take the exact
+//    form).
+//  * u is requested when a wave's last scans are done (its latency overlaps
+//    the final barrier); y = u * sum leaves as 16-byte non-temporal stores.
+//  * 8 waves and 66 KB of LDS per workgroup, one workgroup per CU at two
+//    waves per SIMD (the column directions' pieces in flight need the
+//    registers).
+#include "gspn_device.h"
+#include "gspn_kernels.h"
+
+namespace gspn {
+namespace {
+
+constexpr int kSliceMax = 128;            // largest side
+constexpr int kAccPitch = kSliceMax + 1;  // floats per LDS row of the sum (odd: column accesses spread over banks)
+constexpr int kWaves = 8;
+constexpr int kSliceThreads = 64 * kWaves;
+constexpr int kRowDepth = 4;              // lines loaded ahead by the row directions
+constexpr int kColChunk = 8;              // columns per 16-byte piece read by the column directions
+constexpr int kUVecs = kSliceMax * kSliceMax / 8 / kSliceThreads;   // u vectors per thread
+
+struct SliceParams {
+    const uint16_t* x;
+    const uint16_t* w;
+    const uint16_t* lam;
+    const uint16_t* u;
+    uint16_t* y;
+    int B, C, H, W, Cw, cpw, groups;
+    uint32_t dirs;
+};
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+__device__ __forceinline__ float bf16_at(const uint4& v, int e) {
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+// Weights of the lane's two positions.  Raw taps that are missing or
+// belong to an idle position are 0 here (finite), as normalise_fast needs.
+__device__ __forceinline__ void weights2(const float (&a0)[2], const float (&a1)[2], const float (&a2)[2],
+                                         const bool (&h0)[2], const bool (&h2)[2], float (&w0)[2], float (&w2)[2]) {
+    const float amin = fminf(fminf(fminf(a0[0], a1[0]), a2[0]), fminf(fminf(a0[1], a1[1]), a2[1]));
+    if (__builtin_amdgcn_ballot_w64(amin < -40.0f) == 0) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float2 w = normalise_fast(a0[e], a1[e], a2[e], h0[e], h2[e]);
+            w0[e] = w.x;
+            w2[e] = w.y;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const Taps t = normalise_taps(a0[e], a1[e], a2[e], h0[e], h2[e]);
+            w0[e] = t.w0;
+            w2[e] = t.w2;
+        }
+    }
+}
+
+// One line step of the lane's two positions (the middle weight is
+// 1 - w0 - w2: h' = (h + xl) + w0 (h[p-1] - h) + w2 (h[p+1] - h)).
+__device__ __forceinline__ void step2(float (&h)[2], const float (&xl)[2], const float (&w0)[2],
+                                      const float (&w2)[2]) {
+    const float left = from_left(h[1]);    // position 2l - 1 (lane l - 1)
+    const float right = from_right(h[0]);  // position 2l + 2 (lane l + 1)
+    const float n0 = fmaf(w2[0], h[1] - h[0], fmaf(w0[0], left - h[0], h[0] + xl[0]));
+    const float n1 = fmaf(w2[1], right - h[1], fmaf(w0[1], h[0] - h[1], h[1] + xl[1]));
+    h[0] = n0;
+    h[1] = n1;
+}
+
+// Two waves per SIMD (one workgroup per CU): the column directions keep
+// two 8-column pieces of each input in flight per lane.
+__global__ __attribute__((amdgpu_flat_work_group_size(kSliceThreads, kSliceThreads), amdgpu_waves_per_eu(2, 2)))
+void slice_scan_kernel(SliceParams prm) {
+    __shared__ float acc[kSliceMax * kAccPitch];
+    const int tid = threadIdx.x;
+    const int wave = uniform(tid >> 6), lane = tid & 63;
+    const int H = prm.H, W = prm.W, C = prm.C, B = prm.B;
+    const size_t HW = (size_t)H * W;
+    const int slice = blockIdx.x;
+    const int c = slice % C, b = slice / C;
+    const int k = c / prm.cpw;
+    const uint16_t* __restrict__ xs = prm.x + (size_t)slice * HW;
+    const uint16_t* __restrict__ ls = prm.lam + (size_t)slice * HW;
+    const uint16_t* __restrict__ us = prm.u + (size_t)slice * HW;
+    uint16_t* __restrict__ ys = prm.y + (size_t)slice * HW;
+    const int nvec = (int)(HW / 8);
+
+    const uint32_t dirs = prm.dirs;
+    const int last = 31 - __builtin_clz(dirs);
+    uint4 uu[kUVecs];   // u of the slice, requested when the last direction's scans are done
+    const int first = __builtin_ctz(dirs);
+    // LR and RL over 16-column groups run back to back per group (one wave,
+    // its own columns: no barrier between them), sharing the x and lambda
+    // pieces and with all pieces of both in flight at once
+    const bool both_cols = (dirs & 12u) == 12u && W / prm.groups == 2 * kColChunk;
+    const int u_dir = both_cols && last == 3 ? 2 : last;   // the direction after whose scans u is requested
+    int slot = 0;
+    for (int d = 0; d < 4; ++d) {
+        if (!((dirs >> d) & 1u)) continue;
+        const bool store = d == first;
+        const uint16_t* __restrict__ ws = prm.w + ((size_t)(slot * B + b) * prm.Cw + k) * 3 * HW;
+        ++slot;
+        if (d == 3 && both_cols) continue;   // done with LR
+        if (d == 2 && both_cols) {
+            const uint16_t* __restrict__ ws_rl = ws + (size_t)B * prm.Cw * 3 * HW;   // the next slab
+            const int r0 = 2 * lane;
+            const bool on = r0 < H;
+            const int rc = on ? r0 : H - 2;
+            const bool h0[2] = {on && r0 >= 1, on};
+            const bool h2[2] = {on, on && r0 + 2 < H};
+            const int L = 2 * kColChunk;
+            for (int gi = wave; gi < prm.groups; gi += kWaves) {
+                const int c_base = gi * L;
+                uint4 qa[2][2][5];   // [chunk][row][tap 0, 1, 2 of LR, x, lambda]
+                uint4 qb[2][2][3];   // [chunk][row][tap 0, 1, 2 of RL]
+#pragma unroll
+                for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const size_t o = (size_t)(rc + e) * W + c_base + kColChunk * ch;
+                        qa[ch][e][0] = *reinterpret_cast<const uint4*>(ws + o);
+                        qa[ch][e][1] = *reinterpret_cast<const uint4*>(ws + HW + o);
+                        qa[ch][e][2] = *reinterpret_cast<const uint4*>(ws + 2 * HW + o);
+                        qa[ch][e][3] = *reinterpret_cast<const uint4*>(xs + o);
+                        qa[ch][e][4] = *reinterpret_cast<const uint4*>(ls + o);
+                    }
+#pragma unroll
+                for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const size_t o = (size_t)(rc + e) * W + c_base + kColChunk * ch;
+                        qb[ch][e][0] = *reinterpret_cast<const uint4*>(ws_rl + o);
+                        qb[ch][e][1] = *reinterpret_cast<const uint4*>(ws_rl + HW + o);
+                        qb[ch][e][2] = *reinterpret_cast<const uint4*>(ws_rl + 2 * HW + o);
+                    }
+                // one line of either direction: column index cl in 0 .. 15 of
+                // the group, taps from tp, x and lambda from qa
+                auto line = [&](float (&h)[2], const uint4 (&tp)[2][2][3], auto clc, bool first_line, bool st) {
+                    constexpr int cl = decltype(clc)::value;
+                    constexpr int ch = cl / kColChunk, j = cl % kColChunk;
+                    float xl[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) xl[e] = on ? bf16_at(qa[ch][e][3], j) * bf16_at(qa[ch][e][4], j) : 0.0f;
+                    if (first_line) {
+                        h[0] = xl[0];
+                        h[1] = xl[1];
+                    } else {
+                        float a0[2], a1[2], a2[2], w0[2], w2[2];
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            a0[e] = h0[e] ? bf16_at(tp[ch][e][0], j) : 0.0f;
+                            a1[e] = on ? bf16_at(tp[ch][e][1], j) : 0.0f;
+                            a2[e] = h2[e] ? bf16_at(tp[ch][e][2], j) : 0.0f;
+                        }
+                        weights2(a0, a1, a2, h0, h2, w0, w2);
+                        step2(h, xl, w0, w2);
+                    }
+                    if (on) {
+                        float* dst = acc + r0 * kAccPitch + c_base + cl;
+                        if (st) {
+                            dst[0] = h[0];
+                            dst[kAccPitch] = h[1];
+                        } else {
+                            dst[0] += h[0];
+                            dst[kAccPitch] += h[1];
+                        }
+                    }
+                };
+                uint4 ta[2][2][3];
+#pragma unroll
+                for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+#pragma unroll
+                        for (int t = 0; t < 3; ++t) ta[ch][e][t] = qa[ch][e][t];
+                float h[2] = {0.0f, 0.0f};
+                static_for<0, 2 * kColChunk>([&](auto ic) {            // LR: columns ascending
+                    constexpr int i = decltype(ic)::value;
+                    line(h, ta, std::integral_constant<int, i>{}, i == 0, store);
+                });
+                static_for<0, 2 * kColChunk>([&](auto ic) {            // RL: columns descending
+                    constexpr int i = decltype(ic)::value;
+                    line(h, qb, std::integral_constant<int, 2 * kColChunk - 1 - i>{}, i == 0, false);
+                });
+            }
+        } else if (d < 2) {
+            // ---- row direction: line = row, position = column (lane: 2l, 2l + 1)
+            const int L = H / prm.groups;
+            const int q0 = 2 * lane;
+            const bool on = q0 < W;
+            const int qc = on ? q0 : W - 2;
+            const bool h0[2] = {on && q0 >= 1, on};
+            const bool h2[2] = {on, on && q0 + 2 < W};
+            auto rows = [&](auto asc_c) {
+                constexpr bool kAsc = decltype(asc_c)::value;
+                for (int gi = wave; gi < prm.groups; gi += kWaves) {
+                    const int r_base = gi * L;
+                    auto row_of = [&](int i) { return r_base + (kAsc ? i : L - 1 - i); };
+                    uint32_t ring[kRowDepth][5];   // 3 taps, x, lambda: two bf16 each
+                    auto load = [&](uint32_t (&q)[5], int i) {
+                        const size_t o = (size_t)row_of(min(i, L - 1)) * W + qc;
+                        q[0] = *reinterpret_cast<const uint32_t*>(ws + o);
+                        q[1] = *reinterpret_cast<const uint32_t*>(ws + HW + o);
+                        q[2] = *reinterpret_cast<const uint32_t*>(ws + 2 * HW + o);
+                        q[3] = *reinterpret_cast<const uint32_t*>(xs + o);
+                        q[4] = *reinterpret_cast<const uint32_t*>(ls + o);
+                    };
+#pragma unroll
+                    for (int s = 0; s < kRowDepth; ++s) load(ring[s], s);
+                    float h[2] = {0.0f, 0.0f};
+                    // kRowDepth lines per iteration; steps past the group's last
+                    // line compute on clamped data and store nothing
+                    for (int i0 = 0; i0 < L; i0 += kRowDepth) {
+#pragma unroll
+                        for (int s = 0; s < kRowDepth; ++s) {
+                            const int i = i0 + s;
+                            const uint32_t* q = ring[s];
+                            float xl[2];
+                            xl[0] = on ? bf16_lo(q[3]) * bf16_lo(q[4]) : 0.0f;
+                            xl[1] = on ? bf16_hi(q[3]) * bf16_hi(q[4]) : 0.0f;
+                            if (i == 0) {   // the group's first line: h = lambda x
+                                h[0] = xl[0];
+                                h[1] = xl[1];
+                            } else {
+                                const float a0[2] = {h0[0] ? bf16_lo(q[0]) : 0.0f, h0[1] ? bf16_hi(q[0]) : 0.0f};
+                                const float a1[2] = {on ? bf16_lo(q[1]) : 0.0f, on ? bf16_hi(q[1]) : 0.0f};
+                                const float a2[2] = {h2[0] ? bf16_lo(q[2]) : 0.0f, h2[1] ? bf16_hi(q[2]) : 0.0f};
+                                float w0[2], w2[2];
+                                weights2(a0, a1, a2, h0, h2, w0, w2);
+                                step2(h, xl, w0, w2);
+                            }
+                            if (i < L && on) {
+                                float* dst = acc + row_of(i) * kAccPitch + q0;
+                                if (store) {
+                                    dst[0] = h[0];
+                                    dst[1] = h[1];
+                                } else {
+                                    dst[0] += h[0];
+                                    dst[1] += h[1];
+                                }
+                            }
+                            load(ring[s], i + kRowDepth);
+                        }
+                    }
+                }
+            };
+            if (d == 0) rows(std::true_type{});
+            else rows(std::false_type{});
+        } else {
+            // ---- column direction: line = column, position = row (lane: 2l, 2l + 1)
+            const int L = W / prm.groups;   // a multiple of 4
+            const int nch = L / kColChunk;  // chunks of kColChunk columns
+            const int r0 = 2 * lane;
+            const bool on = r0 < H;
+            const int rc = on ? r0 : H - 2;
+            const bool h0[2] = {on && r0 >= 1, on};
+            const bool h2[2] = {on, on && r0 + 2 < H};
+            auto cols = [&](auto asc_c) {
+                constexpr bool kAsc = decltype(asc_c)::value;
+                for (int gi = wave; gi < prm.groups; gi += kWaves) {
+                    const int c_base = gi * L;
+                    // chunk ch (in scan order) covers columns cols_of(ch) .. + kColChunk
+                    auto cols_of = [&](int ch) { return c_base + kColChunk * (kAsc ? ch : nch - 1 - ch); };
+                    typedef uint4 Chunk[2][5];   // [row 2l, 2l + 1][tap 0, 1, 2, x, lambda]
+                    auto load = [&](Chunk& q, int ch) {
+                        const int cc = cols_of(min(ch, nch - 1));
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const size_t o = (size_t)(rc + e) * W + cc;
+                            q[e][0] = *reinterpret_cast<const uint4*>(ws + o);
+                            q[e][1] = *reinterpret_cast<const uint4*>(ws + HW + o);
+                            q[e][2] = *reinterpret_cast<const uint4*>(ws + 2 * HW + o);
+                            q[e][3] = *reinterpret_cast<const uint4*>(xs + o);
+                            q[e][4] = *reinterpret_cast<const uint4*>(ls + o);
+                        }
+                    };
+                    float h[2] = {0.0f, 0.0f};
+                    auto scan = [&](const Chunk& q, int ch) {
+                        const int cc = cols_of(ch);
+#pragma unroll
+                        for (int t = 0; t < kColChunk; ++t) {
+                            const int j = kAsc ? t : kColChunk - 1 - t;   // column cc + j (compile-time)
+                            float xl[2];
+#pragma unroll
+                            for (int e = 0; e < 2; ++e) xl[e] = on ? bf16_at(q[e][3], j) * bf16_at(q[e][4], j) : 0.0f;
+                            if (ch == 0 && t == 0) {   // the group's first line
+                                h[0] = xl[0];
+                                h[1] = xl[1];
+                            } else {
+                                float a0[2], a1[2], a2[2], w0[2], w2[2];
+#pragma unroll
+                                for (int e = 0; e < 2; ++e) {
+                                    a0[e] = h0[e] ? bf16_at(q[e][0], j) : 0.0f;
+                                    a1[e] = on ? bf16_at(q[e][1], j) : 0.0f;
+                                    a2[e] = h2[e] ? bf16_at(q[e][2], j) : 0.0f;
+                                }
+                                weights2(a0, a1, a2, h0, h2, w0, w2);
+                                step2(h, xl, w0, w2);
+                            }
+                            if (on) {
+                                float* dst = acc + r0 * kAccPitch + cc + j;
+                                if (store) {
+                                    dst[0] = h[0];
+                                    dst[kAccPitch] = h[1];
+                                } else {
+                                    dst[0] += h[0];
+                                    dst[kAccPitch] += h[1];
+                                }
+                            }
+                        }
+                    };
+                    // two chunks in flight: each buffer is refilled after use
+                    Chunk qa, qb;
+                    load(qa, 0);
+                    load(qb, 1);
+                    for (int ch = 0; ch < nch; ch += 2) {
+                        scan(qa, ch);
+                        load(qa, ch + 2);
+                        if (ch + 1 < nch) {
+                            scan(qb, ch + 1);
+                            load(qb, ch + 3);
+                        }
+                    }
+                }
+            };
+            if (d == 2) cols(std::true_type{});
+            else cols(std::false_type{});
+        }
+        if (d == u_dir) {
+#pragma unroll
+            for (int i = 0; i < kUVecs; ++i) {
+                const int v = min(tid + i * kSliceThreads, nvec - 1);
+                uu[i] = *reinterpret_cast<const uint4*>(us + (size_t)v * 8);
+            }
+        }
+        __syncthreads();   // every pixel of this direction is in the sum
+    }
+
+    // ---- y = u * sum
+#pragma unroll
+    for (int i = 0; i < kUVecs; ++i) {
+        const int v = tid + i * kSliceThreads;
+        if (v < nvec) {
+            const int p = v * 8;
+            const int r = p / W, q = p - r * W;
+            const float* s = acc + r * kAccPitch + q;
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = bf16_at(uu[i], e) * s[e];
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 r4 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                              pack_bf16x2(o[6], o[7])};
+            __builtin_nontemporal_store(r4, reinterpret_cast<u32x4*>(ys + p));
+        }
+    }
+}
+
+}  // namespace
+
+bool slice_supported(const ScanArgs& a) {
+    if (!a.bf16 || a.lam_dir || a.u_dir) return false;
+    if (a.H > kSliceMax || a.W > kSliceMax || a.H < 2 || a.W < 8) return false;
+    if (a.W % 8 || a.H % 2) return false;
+    if (a.groups < kWaves) return false;                   // every wave owns a group
+    if ((a.dirs & 12u) && (a.W / a.groups) % kColChunk) return false;   // column groups in 16-byte pieces
+    return true;
+}
+
+hipError_t launch_slice(const ScanArgs& a, hipStream_t stream) {
+    SliceParams p;
+    p.x = static_cast<const uint16_t*>(a.x);
+    p.w = static_cast<const uint16_t*>(a.w);
+    p.lam = static_cast<const uint16_t*>(a.lam);
+    p.u = static_cast<const uint16_t*>(a.u);
+    p.y = static_cast<uint16_t*>(a.y);
+    p.B = a.B; p.C = a.C; p.H = a.H; p.W = a.W; p.Cw = a.C / a.cpw; p.cpw = a.cpw; p.groups = a.groups;
+    p.dirs = a.dirs;
+    hipLaunchKernelGGL(slice_scan_kernel, dim3((unsigned)(a.B * a.C)), dim3(kSliceThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace gspn
+

@@ -86,7 +86,9 @@ def test_groups_only_checked_on_scanned_sides(lib):
 def test_select_path(lib):
     assert gspn.select_path(32, 128, 64, 64, ch_per_weight=8) == gspn.PATH_FUSED
     assert gspn.select_path(1, 8, 32, 32) == gspn.PATH_FUSED
-    assert gspn.select_path(8, 256, 128, 128, groups=8) == gspn.PATH_GENERAL
+    assert gspn.select_path(8, 256, 128, 128, groups=8) == gspn.PATH_SLICE
+    assert gspn.select_path(8, 256, 128, 128, groups=8, dtype=0) == gspn.PATH_GENERAL   # fp32
+    assert gspn.select_path(8, 256, 128, 128, groups=4) == gspn.PATH_GENERAL            # too few groups
     assert gspn.select_path(1, 320, 512, 512) == gspn.PATH_GENERAL
     assert gspn.select_path(1, 8, 32, 32, dirs=0) == -3
 

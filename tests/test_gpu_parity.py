@@ -16,7 +16,7 @@ from linear_spatial_propagation_amd.inputs import (CONFIGS, config_workload, mak
 
 pytestmark = pytest.mark.gpu
 
-PATHS = {"auto": 0, "fused": 1, "general": 2}
+PATHS = {"auto": 0, "fused": 1, "general": 2, "slice": 3}
 
 
 def check(wl, path="auto", tol=None):
@@ -158,3 +158,56 @@ def test_fused_and_line_paths_agree_to_fp32_rounding():
     between = float((np.abs(y1 - y2) / scale).max())
     say(f"  fused vs line kernels: {between:.3e}")
     assert between <= 64 * 2.0 ** -24 * 4
+
+
+# ------------------------------------------------------------ slice kernel
+# one workgroup per (b, c) slice, the sum of the directions in LDS (bf16,
+# H, W <= 128, W % 8 == 0, H even, groups >= 8, (W / groups) % 8 == 0 with
+# LR or RL)
+EDGE_SLICE = [
+    # (B, C, H, W, dirs, groups, cpw)
+    (1, 4, 128, 128, 15, 8, 1),     # the 2K local workload's slices
+    (2, 3, 96, 64, 15, 8, 3),       # 12-line row groups, shared weights
+    (1, 2, 128, 128, 15, 16, 1),    # two groups per wave
+    (1, 2, 128, 128, 3, 32, 2),     # row directions only, 4-line groups
+    (1, 2, 72, 128, 12, 8, 1),      # column directions only, idle lanes
+    (1, 2, 48, 64, 15, 8, 1),       # 6-line row groups, 8-line column groups
+    (1, 2, 128, 64, 9, 8, 1),       # TB and RL
+    (2, 2, 16, 64, 6, 8, 2),        # BT and LR, 2-line row groups
+    (1, 3, 32, 64, 15, 8, 1),       # 4-line row groups, 8-column groups
+    (1, 2, 120, 128, 15, 8, 2),     # 15-line row groups
+]
+
+
+@pytest.mark.parametrize("case", EDGE_SLICE, ids=lambda c: "x".join(map(str, c)))
+def test_edge_shapes_slice(case):
+    B, C, H, W, dirs, g, cpw = case
+    check(make_workload(B, C, H, W, dirs=dirs, groups=g, cpw=cpw, dtype="bf16", seed=sum(case) + 2),
+          path="slice")
+
+
+def test_slice_path_extreme_raw_taps():
+    # raw taps spread over +-250: rows whose taps fall below -40 take the
+    # exact-form normalisation
+    wl = make_workload(1, 4, 128, 128, groups=8, dtype="bf16", seed=91)
+    from linear_spatial_propagation_amd.inputs import bf16_round_bits, bf16_bits_to_f32
+    w = bf16_bits_to_f32(wl.w_store) * np.float32(60.0)
+    w[:, :, :, 1] -= np.float32(120.0)     # whole rows of very negative taps
+    wl.w_store = bf16_round_bits(w)
+    check(wl, path="slice")
+
+
+def test_slice_path_rejects_unsupported_shapes():
+    import torch
+    from linear_spatial_propagation_amd import _lib
+    x = torch.zeros((1, 2, 128, 128), dtype=torch.float32, device="cuda")
+    w = torch.zeros((4, 1, 2, 3, 128, 128), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    # fp32, and too few groups
+    assert _lib.scan_fwd_ptr(x.data_ptr(), w.data_ptr(), x.data_ptr(), x.data_ptr(), y.data_ptr(), 1, 2, 128, 128,
+                             groups=8, dtype=_lib.GSPN_F32, path=3) == -10
+    xb = x.to(torch.bfloat16)
+    wb = w.to(torch.bfloat16)
+    yb = torch.empty_like(xb)
+    assert _lib.scan_fwd_ptr(xb.data_ptr(), wb.data_ptr(), xb.data_ptr(), xb.data_ptr(), yb.data_ptr(), 1, 2, 128,
+                             128, groups=4, path=3) == -10
