@@ -113,9 +113,16 @@ def algorithmic_bytes_bwd(B, C, H, W, dirs, groups, cpw, dtype) -> int:
     return 7 * E * s + fwd_taps + s * nd * B * (C // cpw) * 3 * H * W
 
 
-def kernel_source_hash(pass_="fwd") -> str:
+# sources of the kernels whose counter summaries carry a source hash
+KERNEL_SOURCES = {
+    "slice_scan_kernel": ["linear_spatial_propagation_amd/csrc/gspn_slice.hip",
+                          "linear_spatial_propagation_amd/csrc/gspn_device.h"],
+}
+
+
+def kernel_source_hash(pass_="fwd", kernel=None) -> str:
     h = hashlib.sha256()
-    for rel in PASSES[pass_]["sources"]:
+    for rel in KERNEL_SOURCES[kernel] if kernel in KERNEL_SOURCES else PASSES[pass_]["sources"]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -135,11 +142,13 @@ def _read_summary(path):
     return out
 
 
-def load_traffic(pass_="fwd"):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel source changed since the counters were taken."""
-    t = _read_summary(profile_path(pass_, "traffic"))
-    if t.get("kernel_source_hash") != kernel_source_hash(pass_):
+def load_traffic(pass_="fwd", kernel=None, config="cgspn1k"):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    `kernel` (default: the pass's fused kernel) on `config`, or None when there
+    is none or the kernel source changed since the counters were taken."""
+    kernel = kernel or PASSES[pass_]["kernel"]
+    t = _read_summary(os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.txt"))
+    if t.get("kernel_source_hash") != kernel_source_hash(pass_, kernel):
         return None
     try:
         return int(float(t["hbm_bytes_per_launch"]))
@@ -149,7 +158,8 @@ def load_traffic(pass_="fwd"):
 
 def _kernel_short(name):
     """Short kernel name (the template arguments dropped)."""
-    for k in ("fused_scan_batched_kernel", "fused_scan_kernel", "fused_bwd_kernel", "adjoint_scan_kernel",
+    for k in ("fused_scan_batched_kernel", "fused_scan_kernel", "slice_scan_kernel", "fused_bwd_kernel",
+              "adjoint_scan_kernel",
               "line_scan_kernel", "transpose_kernel", "convert_kernel", "merge_dirs_kernel", "merge_kernel",
               "direction_kernel", "outproj_kernel", "rms_scale_kernel"):
         if k in name:
@@ -192,10 +202,11 @@ def summarize_pmc(pmc_dir, command, config="cgspn1k", pass_="fwd", name=None):
     copy_kib = COPY_CALIBRATION_BYTES / 1024
     f_scale, w_scale = copy_kib / copy_f, copy_kib / copy_w
     c = CONFIGS[config]
-    lines_path = max(c["H"], c["W"]) > 64
-    anchor = ("adjoint_scan_kernel" if lines_path else "fused_bwd_kernel") if pass_ == "bwd" else (
-        "line_scan_kernel" if lines_path else "fused_scan_kernel")
     kernels = sorted({k for (_, k) in vals if k != "copy"})
+    # the kernel run once per step: the single-kernel paths' only kernel, else the line scan
+    anchor = next(k for k in ("fused_scan_kernel", "slice_scan_kernel", "fused_bwd_kernel", "line_scan_kernel",
+                              "adjoint_scan_kernel") if k in kernels)
+    single = anchor in ("fused_scan_kernel", "slice_scan_kernel", "fused_bwd_kernel")
     steps = len(vals[("FETCH_SIZE", anchor)])
     fetch_kib = sum(v for k in kernels for _, v in vals.get(("FETCH_SIZE", k), [])) / steps
     write_kib = sum(v for k in kernels for _, v in vals.get(("WRITE_SIZE", k), [])) / steps
@@ -209,8 +220,8 @@ def summarize_pmc(pmc_dir, command, config="cgspn1k", pass_="fwd", name=None):
         "# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; a step's bytes are the sum over its dispatches;",
         "# each is scaled by (known bytes / counter bytes) of a 256 MiB device-to-device copy in the same run.",
     ]
-    if not lines_path:
-        lines.append(f"kernel_source_hash: {kernel_source_hash(pass_)}")
+    if single:
+        lines.append(f"kernel_source_hash: {kernel_source_hash(pass_, anchor)}")
     lines += [f"steps: {steps}", f"kernels_per_step: {', '.join(kernels)}"]
     for k in kernels:
         fk = sum(v for _, v in vals.get(("FETCH_SIZE", k), [])) / steps
@@ -230,7 +241,7 @@ def summarize_pmc(pmc_dir, command, config="cgspn1k", pass_="fwd", name=None):
         f"algorithmic_bytes_per_launch: {alg}",
         f"traffic_over_algorithmic: {hbm / alg:.4f}",
     ]
-    stem = name or PASSES[pass_]["kernel"]
+    stem = name or (anchor if single else PASSES[pass_]["kernel"])
     with open(os.path.join(ROOT, "profiles", f"{stem}_{config}_traffic.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -258,7 +269,8 @@ def summarize_stats(stats_csv, command, config="cgspn1k", pass_="fwd", name=None
     print("\n".join(lines))
 
 
-GSPN_KERNELS = ("fused_scan_kernel", "fused_scan_batched_kernel", "fused_bwd_kernel", "adjoint_scan_kernel",
+GSPN_KERNELS = ("fused_scan_kernel", "fused_scan_batched_kernel", "slice_scan_kernel", "fused_bwd_kernel",
+                "adjoint_scan_kernel",
                 "line_scan_kernel", "transpose_kernel", "convert_kernel", "merge_kernel", "merge_dirs_kernel",
                 "direction_kernel", "outproj_kernel", "rms_scale_kernel")
 
@@ -709,7 +721,12 @@ def main():
     # roofline: algorithmic bytes over the average step of the timed region
     # (HIP events on the launch stream around the K back-to-back steps)
     achieved = nbytes / (elapsed / args.steps) / 1e9
-    traffic = load_traffic(args.pass_) if args.config == "cgspn1k" and args.variant == "none" else None
+    fwd_path = None if bwd or dirs_variant else gspn.select_path(B, C, H, W, groups=wl.groups, ch_per_weight=wl.cpw)
+    # counter traffic exists for the single-kernel paths (fused forward and backward, slice)
+    traffic_kernel = ("fused_bwd_kernel" if max(H, W) <= 64 else None) if bwd else (
+        {1: "fused_scan_kernel", 3: "slice_scan_kernel"}.get(fwd_path))
+    traffic = (load_traffic(args.pass_, traffic_kernel, args.config)
+               if traffic_kernel and args.variant == "none" and batched == 1 else None)
     E = B * C * H * W
     out = {
         "metric": (METRIC_BWD_DIRS if bwd_variant else METRIC_BWD) if bwd else (METRIC_DIRS if dirs_variant else METRIC),
@@ -731,8 +748,7 @@ def main():
             "path": ("backward line kernels, per-direction lambda and u" if bwd_variant else
                      "fused backward" if max(H, W) <= 64 else "backward line kernels") if bwd else
                     "line kernels, per-direction lambda and u" if dirs_variant else
-                    {1: "fused", 2: "general", 3: "slice"}[gspn.select_path(B, C, H, W, groups=wl.groups,
-                                                                ch_per_weight=wl.cpw)],
+                    {1: "fused", 2: "general", 3: "slice"}[fwd_path],
             "algorithmic_bytes_per_step": nbytes,
             "buffer_sets": R,
             "seed": cfgd["seed"],

@@ -14,23 +14,36 @@
 //    per-direction plane goes through HBM and there is no separate merge
 //    pass: every input is read once and y is written once.
 //  * The directions run one after the other (TB, BT, LR, RL: the fixed
-//    summation order); within a direction, wave w scans groups w, w + 8, ...
+//    summation order; the loop over them is unrolled at compile time so each
+//    direction's registers live only in its own code); within a direction,
+//    wave w scans groups w, w + 8, ...  The first enabled direction reads x
+//    and lambda and leaves lambda x in a second fp32 LDS plane; the others
+//    take it from there, so x and lambda leave HBM once per slice.
 //    Lane l owns positions 2l and 2l + 1 of a line, the state is two VGPRs
 //    and the neighbours across lanes come from DPP wave shifts.  The first
-//    enabled direction stores into the LDS sum, the others add; a barrier
-//    separates the directions.
+//    enabled direction stores into the LDS sum, the others add.  Directions
+//    of one kind give each wave the same lines, so a barrier is needed only
+//    between the row and the column directions and before the output pass.
 //  * Row directions read each line (a row) as 4-byte pieces per lane,
-//    loaded four lines ahead.  Column directions read, for each of the
+//    loaded four lines ahead (a group's first line without its taps, which
+//    the recurrence does not use).  Column directions read, for each of the
 //    lane's two rows, the group's columns as 16-byte pieces of 8 columns:
 //    the eight waves own the groups side by side, so between them they read
 //    whole 128-byte lines at the same time, with no transposed copy.  Two
 //    pieces are in flight ahead of the scan.
+//  * With 16-column groups LR and RL run back to back per group in one
+//    wave, all their pieces (and u's) requested at once; RL, the last
+//    direction, writes y = u * (sum + h) itself as 16-byte pieces, so
+//    there is no output pass and no final barrier.  These are ordinary
+//    stores: the four waves' pieces of a 128-byte line combine in the L2,
+//    where non-temporal ones would reach HBM as partial-line writes (4.5x
+//    the bytes of y).  Otherwise u
+//    is requested after the last direction's scans and a separate pass
+//    writes y.
 //  * Taps are normalised as they are consumed (3 exp + 1 rcp per pixel and
 //    direction, the rational form; rows with a tap below -40 take the exact
 //    form).
-//  * u is requested when a wave's last scans are done (its latency overlaps
-//    the final barrier); y = u * sum leaves as 16-byte non-temporal stores.
-//  * 8 waves and 66 KB of LDS per workgroup, one workgroup per CU at two
+//  * 8 waves and 129 KB of LDS per workgroup, one workgroup per CU at two
 //    waves per SIMD (the column directions' pieces in flight need the
 //    registers).
 #include "gspn_device.h"
@@ -110,6 +123,7 @@ __device__ __forceinline__ void step2(float (&h)[2], const float (&xl)[2], const
 __global__ __attribute__((amdgpu_flat_work_group_size(kSliceThreads, kSliceThreads), amdgpu_waves_per_eu(2, 2)))
 void slice_scan_kernel(SliceParams prm) {
     __shared__ float acc[kSliceMax * kAccPitch];
+    __shared__ float xlp[kSliceMax * kAccPitch];   // lambda * x, written by the first direction
     const int tid = threadIdx.x;
     const int wave = uniform(tid >> 6), lane = tid & 63;
     const int H = prm.H, W = prm.W, C = prm.C, B = prm.B;
@@ -131,96 +145,165 @@ void slice_scan_kernel(SliceParams prm) {
     // its own columns: no barrier between them), sharing the x and lambda
     // pieces and with all pieces of both in flight at once
     const bool both_cols = (dirs & 12u) == 12u && W / prm.groups == 2 * kColChunk;
-    const int u_dir = both_cols && last == 3 ? 2 : last;   // the direction after whose scans u is requested
+    // with the pair, RL is the last direction and writes y = u * sum itself;
+    // otherwise u is requested after the last direction's scans and a
+    // separate pass writes y
+    const bool fused_out = both_cols;
+    const int u_dir = fused_out ? -1 : last;
+    // the pair's pieces of a 16-column group: taps of LR and RL, and u
+    typedef uint4 Taps3[2][2][3];   // [chunk][row 2l, 2l + 1][tap]
+    const int prc = 2 * lane < H ? 2 * lane : H - 2;
+    const uint16_t* __restrict__ ws_lr =
+        prm.w + ((size_t)(__builtin_popcount(dirs & 3u) * B + b) * prm.Cw + k) * 3 * HW;
+    const uint16_t* __restrict__ ws_rl = ws_lr + (size_t)B * prm.Cw * 3 * HW;   // the next slab
+    auto load_pair = [&](int gi, Taps3& ta, Taps3& tb, uint4 (&tu)[2][2]) {
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const size_t o = (size_t)(prc + e) * W + gi * 2 * kColChunk + kColChunk * ch;
+#pragma unroll
+                for (int t = 0; t < 3; ++t) ta[ch][e][t] = *reinterpret_cast<const uint4*>(ws_lr + t * HW + o);
+            }
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const size_t o = (size_t)(prc + e) * W + gi * 2 * kColChunk + kColChunk * ch;
+#pragma unroll
+                for (int t = 0; t < 3; ++t) tb[ch][e][t] = *reinterpret_cast<const uint4*>(ws_rl + t * HW + o);
+            }
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                tu[ch][e] = *reinterpret_cast<const uint4*>(us + (size_t)(prc + e) * W + gi * 2 * kColChunk +
+                                                            kColChunk * ch);
+    };
     int slot = 0;
-    for (int d = 0; d < 4; ++d) {
-        if (!((dirs >> d) & 1u)) continue;
+    static_for<0, 4>([&](auto dc) {   // unrolled: each direction's registers live only in its own code
+        constexpr int d = decltype(dc)::value;
+        if (!((dirs >> d) & 1u)) return;
         const bool store = d == first;
         const uint16_t* __restrict__ ws = prm.w + ((size_t)(slot * B + b) * prm.Cw + k) * 3 * HW;
         ++slot;
-        if (d == 3 && both_cols) continue;   // done with LR
+        if (d == 3 && both_cols) return;   // done with LR
         if (d == 2 && both_cols) {
-            const uint16_t* __restrict__ ws_rl = ws + (size_t)B * prm.Cw * 3 * HW;   // the next slab
             const int r0 = 2 * lane;
             const bool on = r0 < H;
             const int rc = on ? r0 : H - 2;
             const bool h0[2] = {on && r0 >= 1, on};
             const bool h2[2] = {on, on && r0 + 2 < H};
             const int L = 2 * kColChunk;
-            for (int gi = wave; gi < prm.groups; gi += kWaves) {
-                const int c_base = gi * L;
-                uint4 qa[2][2][5];   // [chunk][row][tap 0, 1, 2 of LR, x, lambda]
-                uint4 qb[2][2][3];   // [chunk][row][tap 0, 1, 2 of RL]
+            auto pair = [&](auto first_c) {
+                constexpr bool kFirst = decltype(first_c)::value;   // x and lambda from memory (LR is the first direction)
+                constexpr int kQ = kFirst ? 5 : 3;
+                for (int gi = wave; gi < prm.groups; gi += kWaves) {
+                    const int c_base = gi * L;
+                    uint4 qa[2][2][kQ];   // [chunk][row][tap 0, 1, 2 of LR (, x, lambda)]
+                    uint4 qb[2][2][3];    // [chunk][row][tap 0, 1, 2 of RL]
+                    uint4 uq[2][2];       // [chunk][row] u, for RL's output
+                    if constexpr (kFirst) {
 #pragma unroll
-                for (int ch = 0; ch < 2; ++ch)
+                        for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const size_t o = (size_t)(rc + e) * W + c_base + kColChunk * ch;
-                        qa[ch][e][0] = *reinterpret_cast<const uint4*>(ws + o);
-                        qa[ch][e][1] = *reinterpret_cast<const uint4*>(ws + HW + o);
-                        qa[ch][e][2] = *reinterpret_cast<const uint4*>(ws + 2 * HW + o);
-                        qa[ch][e][3] = *reinterpret_cast<const uint4*>(xs + o);
-                        qa[ch][e][4] = *reinterpret_cast<const uint4*>(ls + o);
-                    }
+                            for (int e = 0; e < 2; ++e) {
+                                const size_t o = (size_t)(rc + e) * W + c_base + kColChunk * ch;
+                                qa[ch][e][3] = *reinterpret_cast<const uint4*>(xs + o);
+                                qa[ch][e][4] = *reinterpret_cast<const uint4*>(ls + o);
+                            }
+                        Taps3 ta3;
+                        load_pair(gi, ta3, qb, uq);
 #pragma unroll
-                for (int ch = 0; ch < 2; ++ch)
+                        for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const size_t o = (size_t)(rc + e) * W + c_base + kColChunk * ch;
-                        qb[ch][e][0] = *reinterpret_cast<const uint4*>(ws_rl + o);
-                        qb[ch][e][1] = *reinterpret_cast<const uint4*>(ws_rl + HW + o);
-                        qb[ch][e][2] = *reinterpret_cast<const uint4*>(ws_rl + 2 * HW + o);
-                    }
-                // one line of either direction: column index cl in 0 .. 15 of
-                // the group, taps from tp, x and lambda from qa
-                auto line = [&](float (&h)[2], const uint4 (&tp)[2][2][3], auto clc, bool first_line, bool st) {
-                    constexpr int cl = decltype(clc)::value;
-                    constexpr int ch = cl / kColChunk, j = cl % kColChunk;
-                    float xl[2];
+                            for (int e = 0; e < 2; ++e)
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) xl[e] = on ? bf16_at(qa[ch][e][3], j) * bf16_at(qa[ch][e][4], j) : 0.0f;
-                    if (first_line) {
-                        h[0] = xl[0];
-                        h[1] = xl[1];
+                                for (int t = 0; t < 3; ++t) qa[ch][e][t] = ta3[ch][e][t];
                     } else {
-                        float a0[2], a1[2], a2[2], w0[2], w2[2];
-#pragma unroll
-                        for (int e = 0; e < 2; ++e) {
-                            a0[e] = h0[e] ? bf16_at(tp[ch][e][0], j) : 0.0f;
-                            a1[e] = on ? bf16_at(tp[ch][e][1], j) : 0.0f;
-                            a2[e] = h2[e] ? bf16_at(tp[ch][e][2], j) : 0.0f;
-                        }
-                        weights2(a0, a1, a2, h0, h2, w0, w2);
-                        step2(h, xl, w0, w2);
+                        load_pair(gi, qa, qb, uq);
                     }
-                    if (on) {
-                        float* dst = acc + r0 * kAccPitch + c_base + cl;
-                        if (st) {
-                            dst[0] = h[0];
-                            dst[kAccPitch] = h[1];
+                    float ov[2][2][kColChunk];   // [chunk][row][column] y of RL's current piece
+                    // one line of either direction: column index cl in 0 .. 15 of
+                    // the group, taps from tp
+                    // mode: 0 stores h into the sum, 1 adds it, 2 writes y = u * (sum + h)
+                    auto line = [&](float (&h)[2], const uint4 (&tp)[2][2][3], auto clc, bool first_line,
+                                    auto mode_c) {
+                        constexpr int cl = decltype(clc)::value;
+                        constexpr int kMode = decltype(mode_c)::value;
+                        constexpr int ch = cl / kColChunk, j = cl % kColChunk;
+                        float xl[2];
+                        if constexpr (kFirst) {
+#pragma unroll
+                            for (int e = 0; e < 2; ++e)
+                                xl[e] = on ? bf16_at(qa[ch][e][3], j) * bf16_at(qa[ch][e][4], j) : 0.0f;
                         } else {
-                            dst[0] += h[0];
-                            dst[kAccPitch] += h[1];
+#pragma unroll
+                            for (int e = 0; e < 2; ++e) xl[e] = on ? xlp[(r0 + e) * kAccPitch + c_base + cl] : 0.0f;
                         }
-                    }
-                };
-                uint4 ta[2][2][3];
+                        if (first_line) {
+                            h[0] = xl[0];
+                            h[1] = xl[1];
+                        } else {
+                            float a0[2], a1[2], a2[2], w0[2], w2[2];
 #pragma unroll
-                for (int ch = 0; ch < 2; ++ch)
+                            for (int e = 0; e < 2; ++e) {
+                                a0[e] = h0[e] ? bf16_at(tp[ch][e][0], j) : 0.0f;
+                                a1[e] = on ? bf16_at(tp[ch][e][1], j) : 0.0f;
+                                a2[e] = h2[e] ? bf16_at(tp[ch][e][2], j) : 0.0f;
+                            }
+                            weights2(a0, a1, a2, h0, h2, w0, w2);
+                            step2(h, xl, w0, w2);
+                        }
+                        float* dst = acc + r0 * kAccPitch + c_base + cl;
+                        if constexpr (kMode == 2) {
 #pragma unroll
-                    for (int e = 0; e < 2; ++e)
+                            for (int e = 0; e < 2; ++e) ov[ch][e][j] = bf16_at(uq[ch][e], j) * (dst[e * kAccPitch] + h[e]);
+                            if (j == 0 && on) {   // the piece is complete (RL runs its columns descending)
+                                typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-                        for (int t = 0; t < 3; ++t) ta[ch][e][t] = qa[ch][e][t];
-                float h[2] = {0.0f, 0.0f};
-                static_for<0, 2 * kColChunk>([&](auto ic) {            // LR: columns ascending
-                    constexpr int i = decltype(ic)::value;
-                    line(h, ta, std::integral_constant<int, i>{}, i == 0, store);
-                });
-                static_for<0, 2 * kColChunk>([&](auto ic) {            // RL: columns descending
-                    constexpr int i = decltype(ic)::value;
-                    line(h, qb, std::integral_constant<int, 2 * kColChunk - 1 - i>{}, i == 0, false);
-                });
-            }
+                                for (int e = 0; e < 2; ++e) {
+                                    const u32x4 r4 = {pack_bf16x2(ov[ch][e][0], ov[ch][e][1]),
+                                                      pack_bf16x2(ov[ch][e][2], ov[ch][e][3]),
+                                                      pack_bf16x2(ov[ch][e][4], ov[ch][e][5]),
+                                                      pack_bf16x2(ov[ch][e][6], ov[ch][e][7])};
+                                    // an ordinary store: the pieces of one 128-byte line come from
+                                    // four waves and merge in the L2 (non-temporal ones would
+                                    // each reach HBM as a partial-line write)
+                                    *reinterpret_cast<u32x4*>(ys + (size_t)(r0 + e) * W + c_base + kColChunk * ch) = r4;
+                                }
+                            }
+                        } else if (on) {
+                            if constexpr (kMode == 0) {
+                                dst[0] = h[0];
+                                dst[kAccPitch] = h[1];
+                            } else {
+                                dst[0] += h[0];
+                                dst[kAccPitch] += h[1];
+                            }
+                        }
+                    };
+                    uint4 ta[2][2][3];
+#pragma unroll
+                    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                        for (int e = 0; e < 2; ++e)
+#pragma unroll
+                            for (int t = 0; t < 3; ++t) ta[ch][e][t] = qa[ch][e][t];
+                    float h[2] = {0.0f, 0.0f};
+                    static_for<0, 2 * kColChunk>([&](auto ic) {            // LR: columns ascending
+                        constexpr int i = decltype(ic)::value;
+                        line(h, ta, std::integral_constant<int, i>{}, i == 0, std::integral_constant<int, kFirst ? 0 : 1>{});
+                    });
+                    static_for<0, 2 * kColChunk>([&](auto ic) {            // RL: columns descending
+                        constexpr int i = decltype(ic)::value;
+                        line(h, qb, std::integral_constant<int, 2 * kColChunk - 1 - i>{}, i == 0,
+                             std::integral_constant<int, 2>{});
+                    });
+                }
+            };
+            if (store) pair(std::true_type{});
+            else pair(std::false_type{});
         } else if (d < 2) {
             // ---- row direction: line = row, position = column (lane: 2l, 2l + 1)
             const int L = H / prm.groups;
@@ -229,22 +312,32 @@ void slice_scan_kernel(SliceParams prm) {
             const int qc = on ? q0 : W - 2;
             const bool h0[2] = {on && q0 >= 1, on};
             const bool h2[2] = {on, on && q0 + 2 < W};
-            auto rows = [&](auto asc_c) {
+            auto rows = [&](auto asc_c, auto first_c) {
                 constexpr bool kAsc = decltype(asc_c)::value;
+                // the first direction reads x and lambda and leaves lambda x in
+                // LDS for the others
+                constexpr bool kFirst = decltype(first_c)::value;
+                constexpr int kQ = kFirst ? 5 : 3;
                 for (int gi = wave; gi < prm.groups; gi += kWaves) {
                     const int r_base = gi * L;
                     auto row_of = [&](int i) { return r_base + (kAsc ? i : L - 1 - i); };
-                    uint32_t ring[kRowDepth][5];   // 3 taps, x, lambda: two bf16 each
-                    auto load = [&](uint32_t (&q)[5], int i) {
+                    uint32_t ring[kRowDepth][kQ];   // 3 taps (, x, lambda): two bf16 each
+                    auto load = [&](uint32_t (&q)[kQ], int i, bool taps = true) {
                         const size_t o = (size_t)row_of(min(i, L - 1)) * W + qc;
-                        q[0] = *reinterpret_cast<const uint32_t*>(ws + o);
-                        q[1] = *reinterpret_cast<const uint32_t*>(ws + HW + o);
-                        q[2] = *reinterpret_cast<const uint32_t*>(ws + 2 * HW + o);
-                        q[3] = *reinterpret_cast<const uint32_t*>(xs + o);
-                        q[4] = *reinterpret_cast<const uint32_t*>(ls + o);
+                        if (taps) {
+                            q[0] = *reinterpret_cast<const uint32_t*>(ws + o);
+                            q[1] = *reinterpret_cast<const uint32_t*>(ws + HW + o);
+                            q[2] = *reinterpret_cast<const uint32_t*>(ws + 2 * HW + o);
+                        }
+                        if constexpr (kFirst) {
+                            q[3] = *reinterpret_cast<const uint32_t*>(xs + o);
+                            q[4] = *reinterpret_cast<const uint32_t*>(ls + o);
+                        }
                     };
+                    // the group's first line has no taps (h = lambda x there)
+                    load(ring[0], 0, false);
 #pragma unroll
-                    for (int s = 0; s < kRowDepth; ++s) load(ring[s], s);
+                    for (int s = 1; s < kRowDepth; ++s) load(ring[s], s);
                     float h[2] = {0.0f, 0.0f};
                     // kRowDepth lines per iteration; steps past the group's last
                     // line compute on clamped data and store nothing
@@ -253,9 +346,19 @@ void slice_scan_kernel(SliceParams prm) {
                         for (int s = 0; s < kRowDepth; ++s) {
                             const int i = i0 + s;
                             const uint32_t* q = ring[s];
+                            float* xd = xlp + row_of(min(i, L - 1)) * kAccPitch + q0;
                             float xl[2];
-                            xl[0] = on ? bf16_lo(q[3]) * bf16_lo(q[4]) : 0.0f;
-                            xl[1] = on ? bf16_hi(q[3]) * bf16_hi(q[4]) : 0.0f;
+                            if constexpr (kFirst) {
+                                xl[0] = on ? bf16_lo(q[3]) * bf16_lo(q[4]) : 0.0f;
+                                xl[1] = on ? bf16_hi(q[3]) * bf16_hi(q[4]) : 0.0f;
+                                if (i < L && on) {
+                                    xd[0] = xl[0];
+                                    xd[1] = xl[1];
+                                }
+                            } else {
+                                xl[0] = on ? xd[0] : 0.0f;
+                                xl[1] = on ? xd[1] : 0.0f;
+                            }
                             if (i == 0) {   // the group's first line: h = lambda x
                                 h[0] = xl[0];
                                 h[1] = xl[1];
@@ -269,7 +372,7 @@ void slice_scan_kernel(SliceParams prm) {
                             }
                             if (i < L && on) {
                                 float* dst = acc + row_of(i) * kAccPitch + q0;
-                                if (store) {
+                                if (kFirst) {
                                     dst[0] = h[0];
                                     dst[1] = h[1];
                                 } else {
@@ -282,8 +385,9 @@ void slice_scan_kernel(SliceParams prm) {
                     }
                 }
             };
-            if (d == 0) rows(std::true_type{});
-            else rows(std::false_type{});
+            if (d == 0) rows(std::true_type{}, std::true_type{});   // TB is the first direction when enabled
+            else if (store) rows(std::false_type{}, std::true_type{});
+            else rows(std::false_type{}, std::false_type{});
         } else {
             // ---- column direction: line = column, position = row (lane: 2l, 2l + 1)
             const int L = W / prm.groups;   // a multiple of 4
@@ -293,13 +397,15 @@ void slice_scan_kernel(SliceParams prm) {
             const int rc = on ? r0 : H - 2;
             const bool h0[2] = {on && r0 >= 1, on};
             const bool h2[2] = {on, on && r0 + 2 < H};
-            auto cols = [&](auto asc_c) {
+            auto cols = [&](auto asc_c, auto first_c) {
                 constexpr bool kAsc = decltype(asc_c)::value;
+                constexpr bool kFirst = decltype(first_c)::value;   // x and lambda from memory, lambda x to LDS
+                constexpr int kQ = kFirst ? 5 : 3;
                 for (int gi = wave; gi < prm.groups; gi += kWaves) {
                     const int c_base = gi * L;
                     // chunk ch (in scan order) covers columns cols_of(ch) .. + kColChunk
                     auto cols_of = [&](int ch) { return c_base + kColChunk * (kAsc ? ch : nch - 1 - ch); };
-                    typedef uint4 Chunk[2][5];   // [row 2l, 2l + 1][tap 0, 1, 2, x, lambda]
+                    typedef uint4 Chunk[2][kQ];   // [row 2l, 2l + 1][tap 0, 1, 2 (, x, lambda)]
                     auto load = [&](Chunk& q, int ch) {
                         const int cc = cols_of(min(ch, nch - 1));
 #pragma unroll
@@ -308,8 +414,10 @@ void slice_scan_kernel(SliceParams prm) {
                             q[e][0] = *reinterpret_cast<const uint4*>(ws + o);
                             q[e][1] = *reinterpret_cast<const uint4*>(ws + HW + o);
                             q[e][2] = *reinterpret_cast<const uint4*>(ws + 2 * HW + o);
-                            q[e][3] = *reinterpret_cast<const uint4*>(xs + o);
-                            q[e][4] = *reinterpret_cast<const uint4*>(ls + o);
+                            if constexpr (kFirst) {
+                                q[e][3] = *reinterpret_cast<const uint4*>(xs + o);
+                                q[e][4] = *reinterpret_cast<const uint4*>(ls + o);
+                            }
                         }
                     };
                     float h[2] = {0.0f, 0.0f};
@@ -320,7 +428,15 @@ void slice_scan_kernel(SliceParams prm) {
                             const int j = kAsc ? t : kColChunk - 1 - t;   // column cc + j (compile-time)
                             float xl[2];
 #pragma unroll
-                            for (int e = 0; e < 2; ++e) xl[e] = on ? bf16_at(q[e][3], j) * bf16_at(q[e][4], j) : 0.0f;
+                            for (int e = 0; e < 2; ++e) {
+                                float* xd = xlp + (r0 + e) * kAccPitch + cc + j;
+                                if constexpr (kFirst) {
+                                    xl[e] = on ? bf16_at(q[e][3], j) * bf16_at(q[e][4], j) : 0.0f;
+                                    if (on) *xd = xl[e];
+                                } else {
+                                    xl[e] = on ? *xd : 0.0f;
+                                }
+                            }
                             if (ch == 0 && t == 0) {   // the group's first line
                                 h[0] = xl[0];
                                 h[1] = xl[1];
@@ -337,7 +453,7 @@ void slice_scan_kernel(SliceParams prm) {
                             }
                             if (on) {
                                 float* dst = acc + r0 * kAccPitch + cc + j;
-                                if (store) {
+                                if (kFirst) {
                                     dst[0] = h[0];
                                     dst[kAccPitch] = h[1];
                                 } else {
@@ -361,8 +477,13 @@ void slice_scan_kernel(SliceParams prm) {
                     }
                 }
             };
-            if (d == 2) cols(std::true_type{});
-            else cols(std::false_type{});
+            if (d == 2) {
+                if (store) cols(std::true_type{}, std::true_type{});
+                else cols(std::true_type{}, std::false_type{});
+            } else {
+                if (store) cols(std::false_type{}, std::true_type{});
+                else cols(std::false_type{}, std::false_type{});
+            }
         }
         if (d == u_dir) {
 #pragma unroll
@@ -371,8 +492,16 @@ void slice_scan_kernel(SliceParams prm) {
                 uu[i] = *reinterpret_cast<const uint4*>(us + (size_t)v * 8);
             }
         }
-        __syncthreads();   // every pixel of this direction is in the sum
-    }
+        // a barrier where the next direction reads what other waves wrote:
+        // between row and column directions and before the output pass.
+        // Directions of one kind give each wave the same lines, so between
+        // TB and BT (or LR and RL) a wave only reads its own LDS writes.
+
+        const uint32_t later = d == 2 && both_cols ? 0u : dirs & ~((2u << d) - 1u);   // the pair ran RL too
+        const bool next_col = later != 0 && __builtin_ctz(later) >= 2;
+        if (later == 0 ? !fused_out : (d >= 2) != next_col) __syncthreads();
+    });
+    if (fused_out) return;   // RL wrote y
 
     // ---- y = u * sum
 #pragma unroll

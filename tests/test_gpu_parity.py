@@ -176,6 +176,12 @@ EDGE_SLICE = [
     (2, 2, 16, 64, 6, 8, 2),        # BT and LR, 2-line row groups
     (1, 3, 32, 64, 15, 8, 1),       # 4-line row groups, 8-column groups
     (1, 2, 120, 128, 15, 8, 2),     # 15-line row groups
+    (1, 2, 128, 64, 3, 8, 1),       # TB then BT over 16-row groups, no column direction
+    (2, 2, 128, 128, 7, 8, 2),      # TB, BT, then LR alone over 16-column groups
+    (1, 2, 64, 128, 13, 4 * 2, 1),  # TB, then LR with RL writing the output
+    (1, 2, 64, 64, 12, 8, 1),       # LR first then RL over 8-column groups
+    (1, 2, 32, 128, 8, 8, 1),       # RL alone
+    (1, 2, 128, 128, 4, 16, 1),     # LR alone, 8-column groups
 ]
 
 
