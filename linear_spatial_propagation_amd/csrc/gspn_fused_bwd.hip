@@ -94,7 +94,7 @@ __device__ __forceinline__ uint4 ld_row(const float* p, int nvalid, bool vec) {
 template <typename T, int N>
 __device__ __forceinline__ void st_row(T* p, const float (&v)[N], int nvalid, bool vec) {
     if (vec) {
-        store16_nt(p, v);
+        store16(p, v);
     } else {
         for (int j = 0; j < N; ++j)
             if (j < nvalid) p[j] = from_f32(v[j], (T*)nullptr);

@@ -30,24 +30,17 @@ __device__ __forceinline__ void unpack(uint4 r, float (&o)[8]) {
 __device__ __forceinline__ void unpack(uint4 r, float (&o)[4]) {
     o[0] = __uint_as_float(r.x); o[1] = __uint_as_float(r.y); o[2] = __uint_as_float(r.z); o[3] = __uint_as_float(r.w);
 }
-// 16-byte store of 8 bf16 (rounded to nearest even) or 4 fp32
+// 16-byte store of 8 bf16 (rounded to nearest even) or 4 fp32.  Outputs use
+// these ordinary stores too, not non-temporal ones: a wave's pieces of a
+// 128-byte line may come from two instructions (or two waves) and combine
+// in the L2, where non-temporal partial-line stores each reach HBM as a
+// write of their own.
 __device__ __forceinline__ void store16(uint16_t* p, const float (&v)[8]) {
     *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                                               pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
 }
 __device__ __forceinline__ void store16(float* p, const float (&v)[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-}
-// non-temporal 16-byte store of 8 bf16 (rounded to nearest even) or 4 fp32
-__device__ __forceinline__ void store16_nt(uint16_t* p, const float (&v)[8]) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 r = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-    __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p));
-}
-__device__ __forceinline__ void store16_nt(float* p, const float (&v)[4]) {
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    const f32x4 r = {v[0], v[1], v[2], v[3]};
-    __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(p));
 }
 
 // ---------------------------------------------------------------- transpose
@@ -450,7 +443,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams prm) {
                 unpack(gv[j][e / N], f);
 #pragma unroll
                 for (int q = 0; q < N; ++q) f[q] *= sum[e + q];
-                store16_nt(gout[j] + o + e, f);   // not read again: non-temporal
+                store16(gout[j] + o + e, f);
             }
         }
         return;
@@ -491,7 +484,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams prm) {
             const size_t e = (size_t)r * W + q;
 #pragma unroll
             for (int j = 0; j < NP; ++j)
-                __builtin_nontemporal_store(from_f32(to_f32(gin[j][e]) * sum, (T*)nullptr), gout[j] + e);
+                gout[j][e] = from_f32(to_f32(gin[j][e]) * sum, (T*)nullptr);
         }
     }
 }
@@ -560,7 +553,7 @@ __global__ __launch_bounds__(256) void merge_dirs_kernel(MergeParams prm) {
             float f[N];
 #pragma unroll
             for (int q = 0; q < N; ++q) f[q] = acc[e + q];
-            store16_nt(gy + o + e, f);
+            store16(gy + o + e, f);
         }
         return;
     }
@@ -596,7 +589,7 @@ __global__ __launch_bounds__(256) void merge_dirs_kernel(MergeParams prm) {
 #pragma unroll
     for (int s = 0; s < kTile / 4; ++s) {
         const int r = r0 + ty + 4 * s, q = c0 + tx;
-        if (r < H && q < W) __builtin_nontemporal_store(from_f32(acc[s], (T*)nullptr), gy + (size_t)r * W + q);
+        if (r < H && q < W) gy[(size_t)r * W + q] = from_f32(acc[s], (T*)nullptr);
     }
 }
 

@@ -419,11 +419,11 @@ __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ 
         const float4 v1 = *reinterpret_cast<const float4*>(src + e + 4);
         f[0] = v0.x; f[1] = v0.y; f[2] = v0.z; f[3] = v0.w; f[4] = v1.x; f[5] = v1.y; f[6] = v1.z; f[7] = v1.w;
         if constexpr (sizeof(T) == 2) {
-            store16_nt(dst + e, f);
+            store16(dst + e, f);
         } else {
             const float a[4] = {f[0], f[1], f[2], f[3]}, c[4] = {f[4], f[5], f[6], f[7]};
-            store16_nt(dst + e, a);
-            store16_nt(dst + e + 4, c);
+            store16(dst + e, a);
+            store16(dst + e + 4, c);
         }
         return;
     }
