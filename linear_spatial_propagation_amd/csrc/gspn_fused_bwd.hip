@@ -28,10 +28,12 @@
 //    D_t - sum_v w_v D_v is a cancellation-free expression in E0, E2 and
 //    the weights.
 //  * The prologue also keeps, per pixel, the sum S of the sigmoids of its
-//    existing taps, so that the epilogue gets sigmoid(a_t) = w_t S.  It forms
-//    1 - sigmoid(a_t) as 1 - w_t S below 1/2 and as exp(-a_t) w_t S above (no
-//    cancellation), reading the raw taps again, and writes the tap gradients
-//    of the set once.
+//    existing taps, so that the epilogue gets sigmoid(a_t) = w_t S.  For fp32
+//    gradients it forms 1 - sigmoid(a_t) as 1 - w_t S below 1/2 and as
+//    exp(-a_t) w_t S above (no cancellation), reading the raw taps again; for
+//    bf16 gradients, whose rounding is far coarser than that cancellation,
+//    it uses 1 - w_t S and w1 = 1 - w0 - w2 and reads no tap twice.  The tap
+//    gradients of the set are written once.
 //  * The prologue and the epilogue take 16 slots at a time.  Column
 //    directions read and write a lane's own row as 16-byte vectors; row
 //    directions hold the chunk transposed (lane = slot and 16 positions) so
@@ -633,10 +635,14 @@ void fused_bwd_kernel(FusedBwdParams prm) {
     // since the weights sum to 1, into sums of products with no cancellation:
     //   t = 0: w1 E0 + w2 (E0 - E2);  t = 1: -(w0 E0 + w2 E2);
     //   t = 2: w1 E2 + w0 (E2 - E0)
-    // and ga_t = w_t (1 - s_t) (D_t - sum_v w_v D_v).  Every weight is
-    // formed directly (w1 = s1 / S), and 1 - s_t without cancellation:
-    // 1 - s_t for s_t < 1/2, else exp(-a_t) s_t, with s_t = w_t S; so the raw
-    // taps are read again.  The chunks of 16 slots run unrolled.
+    // and ga_t = w_t (1 - s_t) (D_t - sum_v w_v D_v), with s_t = w_t S.
+    // fp32 gradients: every weight is formed directly (w1 = s1 / S), and
+    // 1 - s_t without cancellation (1 - s_t for s_t < 1/2, else
+    // exp(-a_t) s_t), so the raw taps are read again.  bf16 gradients: their
+    // rounding (2^-9 relative) dwarfs what w1 = 1 - w0 - w2 and 1 - s_t as it
+    // stands lose to cancellation (about one fp32 ulp of 1, absolute), so the
+    // raw taps are not read again.  The chunks of 16 slots run unrolled.
+    constexpr bool kReadTaps = sizeof(T) == 4;
     if (on) {
         T* gwd = static_cast<T*>(prm.gw) + ((size_t)(slab * B + b) * Cw + k) * 3 * (size_t)HW;
         const float kNegLog2e = -1.44269504088896340736f;
@@ -644,19 +650,24 @@ void fused_bwd_kernel(FusedBwdParams prm) {
         // neighbour exists), weights x0, x2, tap sums E0, E2, sigmoid sum S
         auto tap_grads = [&](bool cpl, bool h0, bool h2, const float (&a3)[3], float x0, float x2, float E0,
                              float E2, float S, float (&ga)[3]) __attribute__((always_inline)) {
-            const float av[3] = {cpl && h0 ? a3[0] : 0.0f, cpl ? a3[1] : 0.0f, cpl && h2 ? a3[2] : 0.0f};
-            float ex[3];
-#pragma unroll
-            for (int u = 0; u < 3; ++u) ex[u] = fast_exp2(av[u] * kNegLog2e);   // may be inf
-            // w1 = sigmoid(a1) / S; if every sigmoid underflows, the
-            // weights came from the exact form and w1 = 1 - w0 - w2
-            const float w1d = fast_rcp(1.0f + ex[1]) * fast_rcp(S);
-            const float wv[3] = {x0, S > 1e-30f ? w1d : 1.0f - x0 - x2, x2};
+            float wv[3] = {x0, 1.0f - x0 - x2, x2};
             float om[3];
+            if constexpr (kReadTaps) {
+                const float av[3] = {cpl && h0 ? a3[0] : 0.0f, cpl ? a3[1] : 0.0f, cpl && h2 ? a3[2] : 0.0f};
+                float ex[3];
 #pragma unroll
-            for (int u = 0; u < 3; ++u) {
-                const float sg = wv[u] * S;
-                om[u] = sg < 0.5f ? 1.0f - sg : ex[u] * sg;
+                for (int u = 0; u < 3; ++u) ex[u] = fast_exp2(av[u] * kNegLog2e);   // may be inf
+                // w1 = sigmoid(a1) / S; if every sigmoid underflows, the
+                // weights came from the exact form and w1 = 1 - w0 - w2
+                if (S > 1e-30f) wv[1] = fast_rcp(1.0f + ex[1]) * fast_rcp(S);
+#pragma unroll
+                for (int u = 0; u < 3; ++u) {
+                    const float sg = wv[u] * S;
+                    om[u] = sg < 0.5f ? 1.0f - sg : ex[u] * sg;
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < 3; ++u) om[u] = 1.0f - wv[u] * S;
             }
             const float r0 = fmaf(wv[1], E0, wv[2] * (E0 - E2));
             const float r1 = -fmaf(wv[0], E0, wv[2] * E2);
@@ -681,8 +692,8 @@ void fused_bwd_kernel(FusedBwdParams prm) {
                 const int t = t0 + qi;
                 const int j = line_of(t);
                 const bool cpl = (coupled >> t) & 1u;
-                float a[3][kChunk];
-                load_taps_rows(t0, a);
+                float a[3][kChunk] = {};
+                if constexpr (kReadTaps) load_taps_rows(t0, a);
                 const float* xr = XRw + qi * kXP + qpos;
                 const float* sg = SGw + t * kXP + qpos;
                 float gaf[3][kChunk];
@@ -710,8 +721,8 @@ void fused_bwd_kernel(FusedBwdParams prm) {
                     }
                 }
             } else {
-                float a[3][kChunk];
-                load_taps(t0, a);
+                float a[3][kChunk] = {};
+                if constexpr (kReadTaps) load_taps(t0, a);
                 float gaf[3][kChunk];
 #pragma unroll
                 for (int i = 0; i < kChunk; ++i) {
