@@ -492,6 +492,8 @@ def main():
     ap.add_argument("--block", action="store_true",
                     help="time the compressed block (gspn_block_fwd) on the 1K block workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-others", dest="others", action="store_false",
+                    help="skip the forward timing of the other workloads (the other_workloads object)")
     ap.add_argument("--profile-run", action="store_true",
                     help="warm-up, timed steps and the roofline pass only (no hot pass, copy or CPU leg): "
                          "the run a kernel-trace summary is taken from")
@@ -778,9 +780,63 @@ def main():
         out["roofline"]["kernel"] = ("gspn_scan_bwd_ex, all launches of one call" if bwd_variant else
                                      "fused_bwd_kernel" if max(H, W) <= 64
                                      else "gspn_scan_bwd, all launches of one call")
+    if (not bwd and args.variant == "none" and batched == 1 and not args.profile_run and not args.copy_calibration
+            and args.others):
+        out["other_workloads"] = time_other_workloads(args.config, dev)
     if not args.no_cpu and not args.profile_run and args.variant == "none" and batched == 1:
         out["cpu_baseline"] = cpu_baseline(args.config, backward=bwd)
     print(json.dumps(out), flush=True)
+
+
+def time_other_workloads(skip, dev, warm=5, steps=20):
+    """Forward time of every other workload of the suite, for context: inputs
+    drawn on the device with the workloads' distributions (x ~ N(0, 1),
+    lambda and u ~ U(0, 1), raw taps ~ N(0, 1)); 20 back-to-back calls on one
+    buffer set after 5 untimed ones, HIP events on the launch stream."""
+    import torch
+    import linear_spatial_propagation_amd as gspn
+    from linear_spatial_propagation_amd import _lib
+    from linear_spatial_propagation_amd.inputs import CONFIGS
+    res = {}
+    stream = torch.cuda.current_stream(dev)
+    for name, c in CONFIGS.items():
+        if name == skip or name == "tiny":
+            continue
+        B, C, H, W = c["B"], c["C"], c["H"], c["W"]
+        dt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
+        g = torch.Generator(device=dev)
+        g.manual_seed(c["seed"])
+        nd = 4
+        x = torch.randn((B, C, H, W), generator=g, device=dev, dtype=torch.float32).to(dt)
+        w = torch.randn((nd, B, C // c["cpw"], 3, H, W), generator=g, device=dev, dtype=torch.float32).to(dt)
+        lam = torch.rand((B, C, H, W), generator=g, device=dev, dtype=torch.float32).to(dt)
+        if c["u_ones"]:
+            u = torch.ones((B, C, H, W), device=dev, dtype=dt)
+        else:
+            u = torch.rand((B, C, H, W), generator=g, device=dev, dtype=torch.float32).to(dt)
+        y = torch.empty_like(x)
+
+        def step():
+            gspn.scan_fwd(x, w, lam, u, dirs=15, groups=c["groups"], ch_per_weight=c["cpw"], out=y)
+        for _ in range(warm):
+            step()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        nbytes = algorithmic_bytes(B, C, H, W, 15, c["groups"], c["cpw"], c["dtype"])
+        res[name] = {"path": {1: "fused", 2: "general", 3: "slice"}[
+                         gspn.select_path(B, C, H, W, groups=c["groups"], ch_per_weight=c["cpw"],
+                                          dtype=_lib.GSPN_BF16 if c["dtype"] == "bf16" else _lib.GSPN_F32)],
+                     "us_per_step": round(us, 2), "gbps": round(nbytes / us / 1e3, 1),
+                     "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
+        del x, w, lam, u, y
+        torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":
