@@ -160,10 +160,11 @@ struct LineVec {
     }
 };
 
-// The inputs of one line for one lane: three raw taps, x and lambda.
-template <typename T, int K>
+// The inputs of one line for one lane: three raw taps, and x and lambda of
+// each of the G channels that share the taps.
+template <typename T, int K, int G>
 struct LineData {
-    LineVec<T, K> a[3], x, l;
+    LineVec<T, K> a[3], x[G], l[G];
 };
 
 // D: lines loaded ahead (deeper for long lines: fewer waves share the GPU
@@ -172,18 +173,26 @@ struct LineData {
 // owning 64 K consecutive positions; after every line they swap the state at
 // their common edge through LDS (one barrier per line).  Halving the unit of
 // work balances launches whose scans barely exceed one wave per SIMD.
-template <typename T, int K, int D, int SPLIT>
+// G: channels per wave, G consecutive channels of one weight set (cpw a
+// multiple of G): the taps are loaded and normalised once per pixel and
+// drive the G channels' scans (the channel-shared weights of the GSPN-2
+// author response, "How Channel-shared Weight Mitigates the Concurrency
+// Bottleneck?").  SPLIT = 2 takes G = 1.
+template <typename T, int K, int D, int SPLIT, int G>
 __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
+    static_assert(SPLIT == 1 || G == 1, "split lines scan one channel per wave");
     const int lane = threadIdx.x & 63;
     const int half = SPLIT == 2 ? uniform(threadIdx.x >> 6) : 0;   // which part of the line
     const int unit = SPLIT == 2 ? (int)blockIdx.x : (int)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
     const int C = prm.C, B = prm.B;
-    if (unit >= prm.nd * B * C) return;   // whole wave
-    // (b, c, slot), slot fastest: the directions of one slice run side by
-    // side, so the pair that reads the same x and lambda shares them in cache
+    const int CG = C / G;   // channel groups
+    if (unit >= prm.nd * B * CG) return;   // whole wave
+    // (b, channel group, slot), slot fastest: the directions of one slice run
+    // side by side, so the pair that reads the same x and lambda shares them
+    // in cache
     const int slot = unit % prm.nd;
-    const int c = (unit / prm.nd) % C;
-    const int b = unit / (prm.nd * C);
+    const int c = ((unit / prm.nd) % CG) * G;   // first channel of the group
+    const int b = unit / (prm.nd * CG);
     const int d = prm.dir_of_slot[slot];
     const int k = c / prm.cpw;
     const bool is_row = d < 2;
@@ -194,7 +203,8 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
     const int m = is_row ? W : H;   // positions per line
     const int L = n / prm.groups;
 
-    // every tensor is read as [n][m], line-major
+    // every tensor is read as [n][m], line-major; channel g of the group is
+    // g * HW further on
     const T* xs = static_cast<const T*>(is_row ? prm.x : prm.xT) + ((size_t)b * C + c) * HW;
     const T* ls = (is_row ? static_cast<const T*>(prm.lam) + slot * prm.lam_ds
                           : static_cast<const T*>(prm.lamT) + prm.col_index[slot] * prm.lamT_ds) +
@@ -225,23 +235,28 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
     const float fl = lane_on ? 1.0f : 0.0f;
     auto masked = [](float v, uint32_t msk) { return __uint_as_float(__float_as_uint(v) & msk); };
 
-    auto load_line = [&](LineData<T, K>& q, int i) {
+    auto load_line = [&](LineData<T, K, G>& q, int i) {
         const int j = asc ? i : n - 1 - i;
         const size_t o = (size_t)j * m + pl;
         q.a[0].load(ws + o);
         q.a[1].load(ws + HW + o);
         q.a[2].load(ws + 2 * HW + o);
-        q.x.load(xs + o);
-        q.l.load(ls + o);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            q.x[g].load(xs + g * HW + o);
+            q.l[g].load(ls + g * HW + o);
+        }
     };
 
-    LineData<T, K> buf[D];
+    LineData<T, K, G> buf[D];
 #pragma unroll
     for (int s = 0; s < D; ++s) load_line(buf[s], min(s, n - 1));
 
-    float h[K];
+    float h[G][K];
 #pragma unroll
-    for (int e = 0; e < K; ++e) h[e] = 0.0f;
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < K; ++e) h[g][e] = 0.0f;
     // SPLIT: the neighbour part's state at the common edge (position
     // 64K - 1 or 64K of the line), from the previous line
     __shared__ float edge[2][2];   // [line parity][part]
@@ -255,21 +270,26 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
 #pragma unroll
         for (int s = 0; s < D; ++s) {
             const int i = i0 + s;
-            const LineData<T, K>& q = buf[s];
-            float xl[K], a0[K], a1[K], a2[K];
+            const LineData<T, K, G>& q = buf[s];
+            float xl[G][K], a0[K], a1[K], a2[K];
             float amin = 0.0f;
 #pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < K; ++e) xl[g][e] = masked(q.x[g].get(e), ml) * masked(q.l[g].get(e), ml);
+#pragma unroll
             for (int e = 0; e < K; ++e) {
-                xl[e] = masked(q.x.get(e), ml) * masked(q.l.get(e), ml);
                 a0[e] = masked(q.a[0].get(e), e == 0 ? m0 : ml);   // missing taps -> 0
                 a1[e] = masked(q.a[1].get(e), ml);
                 a2[e] = masked(q.a[2].get(e), e == K - 1 ? m2 : ml);
                 amin = fminf(amin, fminf(fminf(a0[e], a1[e]), a2[e]));
             }
-            float hn[K];
+            float hn[G][K];
             if (i % L == 0) {   // group start: h = lambda x, the taps are unused
 #pragma unroll
-                for (int e = 0; e < K; ++e) hn[e] = xl[e];
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int e = 0; e < K; ++e) hn[g][e] = xl[g][e];
             } else {
                 float w0[K], w2[K];
                 // the rational form is safe when every tap is >= -40
@@ -295,32 +315,37 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
                         w2[e] = tp.w2;
                     }
                 }
-                float left = from_left(h[K - 1]);
-                float right = from_right(h[0]);
-                if constexpr (SPLIT == 2) {
-                    // the lane exchange runs in every lane before the edge
-                    // lanes take the other part's value: sunk into a branch
-                    // it would read the masked-off edge lanes as 0
-                    asm volatile("" : "+v"(left), "+v"(right));
-                    left = takes_left ? bnd : left;
-                    right = takes_right ? bnd : right;
-                }
 #pragma unroll
-                for (int e = 0; e < K; ++e) {
-                    const float hl = e == 0 ? left : h[e - 1];
-                    const float hr = e == K - 1 ? right : h[e + 1];
-                    float v = h[e] + xl[e];
-                    v = fmaf(w0[e], hl - h[e], v);
-                    hn[e] = fmaf(w2[e], hr - h[e], v);
+                for (int g = 0; g < G; ++g) {
+                    float left = from_left(h[g][K - 1]);
+                    float right = from_right(h[g][0]);
+                    if constexpr (SPLIT == 2) {
+                        // the lane exchange runs in every lane before the edge
+                        // lanes take the other part's value: sunk into a branch
+                        // it would read the masked-off edge lanes as 0
+                        asm volatile("" : "+v"(left), "+v"(right));
+                        left = takes_left ? bnd : left;
+                        right = takes_right ? bnd : right;
+                    }
+#pragma unroll
+                    for (int e = 0; e < K; ++e) {
+                        const float hl = e == 0 ? left : h[g][e - 1];
+                        const float hr = e == K - 1 ? right : h[g][e + 1];
+                        float v = h[g][e] + xl[g][e];
+                        v = fmaf(w0[e], hl - h[g][e], v);
+                        hn[g][e] = fmaf(w2[e], hr - h[g][e], v);
+                    }
                 }
             }
 #pragma unroll
-            for (int e = 0; e < K; ++e) h[e] = hn[e];
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < K; ++e) h[g][e] = hn[g][e];
             if constexpr (SPLIT == 2) {
                 // swap the edge states; the parity double-buffers the slots so
                 // that one barrier per line suffices
                 const int par = i & 1;
-                if (lane == (half == 0 ? 63 : 0)) edge[par][half] = half == 0 ? h[K - 1] : h[0];
+                if (lane == (half == 0 ? 63 : 0)) edge[par][half] = half == 0 ? h[0][K - 1] : h[0][0];
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
                 __builtin_amdgcn_s_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -331,15 +356,20 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
                 // makes the counter waits conservative): lanes past the line
                 // and steps past the last line write to a per-lane sink
                 const int j = asc ? i : n - 1 - i;
-                float* dst = (i < n && lane_on) ? plane + (size_t)j * m + p0 : prm.sink + K * lane;
-                if constexpr (K == 1) {
-                    dst[0] = h[0];
-                } else if constexpr (K == 2) {
-                    *reinterpret_cast<float2*>(dst) = make_float2(h[0], h[1]);
-                } else {
+                const bool real = i < n && lane_on;
 #pragma unroll
-                    for (int e = 0; e < K; e += 4)
-                        *reinterpret_cast<float4*>(dst + e) = make_float4(h[e], h[e + 1], h[e + 2], h[e + 3]);
+                for (int g = 0; g < G; ++g) {
+                    float* dst = real ? plane + (size_t)g * HW + (size_t)j * m + p0 : prm.sink + K * lane;
+                    if constexpr (K == 1) {
+                        dst[0] = h[g][0];
+                    } else if constexpr (K == 2) {
+                        *reinterpret_cast<float2*>(dst) = make_float2(h[g][0], h[g][1]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < K; e += 4)
+                            *reinterpret_cast<float4*>(dst + e) =
+                                make_float4(h[g][e], h[g][e + 1], h[g][e + 2], h[g][e + 3]);
+                    }
                 }
             }
             // refill the slot with the line D ahead (clamped: no
@@ -623,17 +653,35 @@ void launch_transpose(const TS* src, TD* dst, size_t planes, int R, int Cc, hipS
                        src, dst, R, Cc, tiles_r, tiles_c);
 }
 
-// one wave per (slot, b, c)
+// Channels per wave of the line scan: 2 when the weight sets have an even
+// number of channels and the halved launch still has at least 8 waves per
+// SIMD (8192 on the 1024 SIMDs of the GPU), else 1.
+inline int line_scan_channels(const LineParams& p) {
+    const long units = (long)p.nd * p.B * p.C;
+    const int m = p.H > p.W ? p.H : p.W;
+    return m <= 256 && p.cpw % 2 == 0 && units / 2 >= 8192 ? 2 : 1;
+}
+
+// one wave per (slot, b, group of G channels)
 template <typename T>
 void launch_line_scan(const LineParams& p, hipStream_t stream) {
     const long units = (long)p.nd * p.B * p.C;
-    const dim3 grid((unsigned)((units + 3) / 4));
     const int m = p.H > p.W ? p.H : p.W;
-    if (m <= 64) hipLaunchKernelGGL((line_scan_kernel<T, 1, kDepth, 1>), grid, dim3(256), 0, stream, p);
-    else if (m <= 128) hipLaunchKernelGGL((line_scan_kernel<T, 2, kDepth, 1>), grid, dim3(256), 0, stream, p);
-    else if (m <= 256) hipLaunchKernelGGL((line_scan_kernel<T, 4, kDepthK4, 1>), grid, dim3(256), 0, stream, p);
-    else   // sides above 256: two waves of 4 positions per lane hold a line
-        hipLaunchKernelGGL((line_scan_kernel<T, 4, kDepthK4, 2>), dim3((unsigned)units), dim3(128), 0, stream, p);
+    if (m > 256) {   // sides above 256: two waves of 4 positions per lane hold a line
+        hipLaunchKernelGGL((line_scan_kernel<T, 4, kDepthK4, 2, 1>), dim3((unsigned)units), dim3(128), 0, stream, p);
+        return;
+    }
+    const int G = line_scan_channels(p);
+    const dim3 grid((unsigned)((units / G + 3) / 4));
+    if (G == 2) {
+        if (m <= 64) hipLaunchKernelGGL((line_scan_kernel<T, 1, kDepth, 1, 2>), grid, dim3(256), 0, stream, p);
+        else if (m <= 128) hipLaunchKernelGGL((line_scan_kernel<T, 2, kDepth, 1, 2>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((line_scan_kernel<T, 4, kDepthK4, 1, 2>), grid, dim3(256), 0, stream, p);
+    } else {
+        if (m <= 64) hipLaunchKernelGGL((line_scan_kernel<T, 1, kDepth, 1, 1>), grid, dim3(256), 0, stream, p);
+        else if (m <= 128) hipLaunchKernelGGL((line_scan_kernel<T, 2, kDepth, 1, 1>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((line_scan_kernel<T, 4, kDepthK4, 1, 1>), grid, dim3(256), 0, stream, p);
+    }
 }
 
 template <typename T>

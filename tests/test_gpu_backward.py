@@ -149,6 +149,34 @@ def test_bwd_config_sampled_sets(name, nsets):
     assert max(worst.values()) <= TOL[wl.dtype], worst
 
 
+def test_bwd_line_path_channel_pairs_sampled_sets():
+    # large enough that the line kernels' forward pass scans two channels of a
+    # weight set per wave
+    B, C, H, W, cpw, seed = 2, 2048, 72, 72, 2, 71
+    say("case bwd line pairs: generating")
+    wl = make_workload(B, C, H, W, groups=1, cpw=cpw, dtype="bf16", seed=seed)
+    gy = make_gy(wl, seed + 1)
+    say("case bwd line pairs: GPU")
+    got = run_bwd(wl, gy)
+    Cw = C // cpw
+    worst = {nm: 0.0 for nm in NAMES}
+    for (b, k) in sampled_sets(B, Cw, 6, 78):
+        chans = range(k * cpw, (k + 1) * cpw)
+        parts = [slice_inputs_f64(seed, b, c, H=H, W=W, dirs=15, cpw=cpw, dtype="bf16") for c in chans]
+        x = np.stack([p[0] for p in parts])[None]
+        w = parts[0][1][:, None, None]
+        lam = np.stack([p[2] for p in parts])[None]
+        u = np.stack([p[3] for p in parts])[None]
+        g = np.stack([gy_f64(gy[b, c], "bf16") for c in chans])[None]
+        want = oracle.scan_bwd(x, w, lam, u, g, dirs=15, groups=1, cpw=cpw)
+        have = (got[0][b, k * cpw:(k + 1) * cpw][None], got[1][:, b, k][:, None, None],
+                got[2][b, k * cpw:(k + 1) * cpw][None], got[3][b, k * cpw:(k + 1) * cpw][None])
+        for nm, v in errors(have, want, "bf16").items():
+            worst[nm] = max(worst[nm], v)
+    say("  worst " + " ".join(f"{k}={v:.3e}" for k, v in worst.items()))
+    assert max(worst.values()) <= TOL["bf16"], worst
+
+
 @pytest.mark.parametrize("path", ["fused", "lines"])
 @pytest.mark.parametrize("scale", [12.0, 60.0])
 def test_bwd_wide_raw_taps(path, scale):

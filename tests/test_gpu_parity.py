@@ -69,6 +69,33 @@ def test_config_sampled_slices(name, nslices):
     assert max(errs) <= TOL[wl.dtype]
 
 
+# Line path with channel-shared weights on launches large enough that each
+# wave scans two channels of one weight set (the halved launch still has at
+# least 8 waves per SIMD): one normalisation per pixel serves both.
+LINE_SHARED = [
+    # (B, C, H, W, dirs, groups, cpw, dtype)
+    (4, 1024, 72, 72, 15, 1, 2, "bf16"),     # 2 positions per lane
+    (4, 1024, 72, 72, 15, 4, 4, "bf16"),     # local groups
+    (2, 2048, 132, 68, 15, 2, 4, "f32"),     # 4 positions per lane, fp32
+]
+
+
+@pytest.mark.parametrize("case", LINE_SHARED, ids=lambda c: "x".join(map(str, c)))
+def test_line_path_channel_pairs_sampled_slices(case):
+    B, C, H, W, dirs, g, cpw, dt = case
+    seed = 40 + H + cpw
+    say(f"case line pairs {case}: generating")
+    wl = make_workload(B, C, H, W, dirs=dirs, groups=g, cpw=cpw, dtype=dt, seed=seed)
+    say(f"case line pairs {case}: GPU")
+    y = run_workload(wl, PATHS["general"])
+    errs = []
+    for (b, c) in sampled_slices(B, C, cpw, 24, seed):
+        x, w, lam, u = slice_inputs_f64(seed, b, c, H=H, W=W, dirs=dirs, cpw=cpw, dtype=dt)
+        errs.append(parity_error(y[b, c], oracle.slice_fwd(x, w, lam, u, dirs=dirs, groups=g), dt))
+    say(f"  max err over {len(errs)} slices = {max(errs):.3e}")
+    assert max(errs) <= TOL[dt]
+
+
 # ------------------------------------------------------------ edge shapes
 EDGE = [
     # (B, C, H, W, dirs, groups, cpw)
