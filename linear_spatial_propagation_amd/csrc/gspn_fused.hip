@@ -571,7 +571,7 @@ __device__ __forceinline__ void fused_scan_body(const FusedParams& prm, const in
         constexpr int kNCh = kS / kChunk;
         constexpr int kLd = TapChunk<T>::kLoads;
 #ifndef GSPN_TAP_AHEAD
-#define GSPN_TAP_AHEAD 2
+#define GSPN_TAP_AHEAD 3
 #endif
 #ifndef GSPN_SLOTS
 #define GSPN_SLOTS 8
