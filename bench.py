@@ -321,9 +321,16 @@ def summarize_trace(trace_csv, command, config, pass_, warmup, steps, name=None)
     lines += part("timed", warmup, steps)
     lines += part("steady", warmup + steps + ROOF_WARM, ROOF_N)
     lines.append(f"algorithmic_bytes_per_step: {alg}")
-    if name is None and config == "cgspn1k":
-        lines.append(f"kernel_source_hash: {kernel_source_hash(pass_)}")
-    stem = name or PASSES[pass_]["kernel"]
+    if name is None:
+        # a step that is one kernel is summarised under that kernel's name,
+        # with the hash of the source it was built from
+        kinds = set(_kernel_short(r["Kernel_Name"]) for r in rows)
+        if len(kinds) != 1:
+            raise SystemExit(f"kernels {sorted(kinds)} in one step: give --profile-name")
+        name = kinds.pop()
+        if name in KERNEL_SOURCES or name == PASSES[pass_]["kernel"]:
+            lines.append(f"kernel_source_hash: {kernel_source_hash(pass_, name)}")
+    stem = name
     out = os.path.join(ROOT, "profiles", f"{stem}_{config}_stats.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")

@@ -31,7 +31,7 @@
 //    the eight waves own the groups side by side, so between them they read
 //    whole 128-byte lines at the same time, with no transposed copy.  Two
 //    pieces are in flight ahead of the scan.
-//  * With 16-column groups LR and RL run back to back per group in one
+//  * With 8- or 16-column groups LR and RL run back to back per group in one
 //    wave, all their pieces (and u's) requested at once; RL, the last
 //    direction, writes y = u * (sum + h) itself as 16-byte pieces, so
 //    there is no output pass and no final barrier.  These are ordinary
@@ -120,6 +120,9 @@ __device__ __forceinline__ void step2(float (&h)[2], const float (&xl)[2], const
 
 // Two waves per SIMD (one workgroup per CU): the column directions keep
 // two 8-column pieces of each input in flight per lane.
+// PNCH: 8-column pieces per group of the LR/RL pair this instantiation
+// holds (1 or 2; one per kernel keeps each kernel's code to its own pair).
+template <int PNCH>
 __global__ __attribute__((amdgpu_flat_work_group_size(kSliceThreads, kSliceThreads), amdgpu_waves_per_eu(2, 2)))
 void slice_scan_kernel(SliceParams prm) {
     __shared__ float acc[kSliceMax * kAccPitch];
@@ -141,43 +144,44 @@ void slice_scan_kernel(SliceParams prm) {
     const int last = 31 - __builtin_clz(dirs);
     uint4 uu[kUVecs];   // u of the slice, requested when the last direction's scans are done
     const int first = __builtin_ctz(dirs);
-    // LR and RL over 16-column groups run back to back per group (one wave,
-    // its own columns: no barrier between them), sharing the x and lambda
-    // pieces and with all pieces of both in flight at once
-    const bool both_cols = (dirs & 12u) == 12u && W / prm.groups == 2 * kColChunk;
+    // LR and RL over 8- or 16-column groups run back to back per group (one
+    // wave, its own columns: no barrier between them), sharing the x and
+    // lambda pieces and with all pieces of both in flight at once
+    const bool both_cols = (dirs & 12u) == 12u && W / prm.groups == PNCH * kColChunk;
     // with the pair, RL is the last direction and writes y = u * sum itself;
     // otherwise u is requested after the last direction's scans and a
     // separate pass writes y
     const bool fused_out = both_cols;
     const int u_dir = fused_out ? -1 : last;
-    // the pair's pieces of a 16-column group: taps of LR and RL, and u
-    typedef uint4 Taps3[2][2][3];   // [chunk][row 2l, 2l + 1][tap]
+    // the pair's pieces of a group of PNCH 8-column pieces: taps of LR and RL,
+    // and u
+    typedef uint4 Taps3[PNCH][2][3];   // [piece][row 2l, 2l + 1][tap]
     const int prc = 2 * lane < H ? 2 * lane : H - 2;
     const uint16_t* __restrict__ ws_lr =
         prm.w + ((size_t)(__builtin_popcount(dirs & 3u) * B + b) * prm.Cw + k) * 3 * HW;
     const uint16_t* __restrict__ ws_rl = ws_lr + (size_t)B * prm.Cw * 3 * HW;   // the next slab
-    auto load_pair = [&](int gi, Taps3& ta, Taps3& tb, uint4 (&tu)[2][2]) {
+    auto load_pair = [&](int gi, Taps3& ta, Taps3& tb, uint4 (&tu)[PNCH][2]) {
 #pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
+        for (int ch = 0; ch < PNCH; ++ch)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const size_t o = (size_t)(prc + e) * W + gi * 2 * kColChunk + kColChunk * ch;
+                const size_t o = (size_t)(prc + e) * W + gi * PNCH * kColChunk + kColChunk * ch;
 #pragma unroll
                 for (int t = 0; t < 3; ++t) ta[ch][e][t] = *reinterpret_cast<const uint4*>(ws_lr + t * HW + o);
             }
 #pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
+        for (int ch = 0; ch < PNCH; ++ch)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const size_t o = (size_t)(prc + e) * W + gi * 2 * kColChunk + kColChunk * ch;
+                const size_t o = (size_t)(prc + e) * W + gi * PNCH * kColChunk + kColChunk * ch;
 #pragma unroll
                 for (int t = 0; t < 3; ++t) tb[ch][e][t] = *reinterpret_cast<const uint4*>(ws_rl + t * HW + o);
             }
 #pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
+        for (int ch = 0; ch < PNCH; ++ch)
 #pragma unroll
             for (int e = 0; e < 2; ++e)
-                tu[ch][e] = *reinterpret_cast<const uint4*>(us + (size_t)(prc + e) * W + gi * 2 * kColChunk +
+                tu[ch][e] = *reinterpret_cast<const uint4*>(us + (size_t)(prc + e) * W + gi * PNCH * kColChunk +
                                                             kColChunk * ch);
     };
     int slot = 0;
@@ -194,18 +198,19 @@ void slice_scan_kernel(SliceParams prm) {
             const int rc = on ? r0 : H - 2;
             const bool h0[2] = {on && r0 >= 1, on};
             const bool h2[2] = {on, on && r0 + 2 < H};
-            const int L = 2 * kColChunk;
+            const int L = PNCH * kColChunk;
+            constexpr int NCH = PNCH;
             auto pair = [&](auto first_c) {
                 constexpr bool kFirst = decltype(first_c)::value;   // x and lambda from memory (LR is the first direction)
                 constexpr int kQ = kFirst ? 5 : 3;
                 for (int gi = wave; gi < prm.groups; gi += kWaves) {
                     const int c_base = gi * L;
-                    uint4 qa[2][2][kQ];   // [chunk][row][tap 0, 1, 2 of LR (, x, lambda)]
-                    uint4 qb[2][2][3];    // [chunk][row][tap 0, 1, 2 of RL]
-                    uint4 uq[2][2];       // [chunk][row] u, for RL's output
+                    uint4 qa[NCH][2][kQ];   // [piece][row][tap 0, 1, 2 of LR (, x, lambda)]
+                    uint4 qb[NCH][2][3];    // [piece][row][tap 0, 1, 2 of RL]
+                    uint4 uq[NCH][2];       // [piece][row] u, for RL's output
                     if constexpr (kFirst) {
 #pragma unroll
-                        for (int ch = 0; ch < 2; ++ch)
+                        for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
                             for (int e = 0; e < 2; ++e) {
                                 const size_t o = (size_t)(rc + e) * W + c_base + kColChunk * ch;
@@ -215,7 +220,7 @@ void slice_scan_kernel(SliceParams prm) {
                         Taps3 ta3;
                         load_pair(gi, ta3, qb, uq);
 #pragma unroll
-                        for (int ch = 0; ch < 2; ++ch)
+                        for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
                             for (int e = 0; e < 2; ++e)
 #pragma unroll
@@ -223,11 +228,11 @@ void slice_scan_kernel(SliceParams prm) {
                     } else {
                         load_pair(gi, qa, qb, uq);
                     }
-                    float ov[2][2][kColChunk];   // [chunk][row][column] y of RL's current piece
-                    // one line of either direction: column index cl in 0 .. 15 of
-                    // the group, taps from tp
+                    float ov[NCH][2][kColChunk];   // [piece][row][column] y of RL's current piece
+                    // one line of either direction: column index cl in 0 .. L - 1
+                    // of the group, taps from tp
                     // mode: 0 stores h into the sum, 1 adds it, 2 writes y = u * (sum + h)
-                    auto line = [&](float (&h)[2], const uint4 (&tp)[2][2][3], auto clc, bool first_line,
+                    auto line = [&](float (&h)[2], const uint4 (&tp)[NCH][2][3], auto clc, bool first_line,
                                     auto mode_c) {
                         constexpr int cl = decltype(clc)::value;
                         constexpr int kMode = decltype(mode_c)::value;
@@ -283,21 +288,21 @@ void slice_scan_kernel(SliceParams prm) {
                             }
                         }
                     };
-                    uint4 ta[2][2][3];
+                    uint4 ta[NCH][2][3];
 #pragma unroll
-                    for (int ch = 0; ch < 2; ++ch)
+                    for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
                         for (int e = 0; e < 2; ++e)
 #pragma unroll
                             for (int t = 0; t < 3; ++t) ta[ch][e][t] = qa[ch][e][t];
                     float h[2] = {0.0f, 0.0f};
-                    static_for<0, 2 * kColChunk>([&](auto ic) {            // LR: columns ascending
+                    static_for<0, PNCH * kColChunk>([&](auto ic) {            // LR: columns ascending
                         constexpr int i = decltype(ic)::value;
                         line(h, ta, std::integral_constant<int, i>{}, i == 0, std::integral_constant<int, kFirst ? 0 : 1>{});
                     });
-                    static_for<0, 2 * kColChunk>([&](auto ic) {            // RL: columns descending
+                    static_for<0, PNCH * kColChunk>([&](auto ic) {            // RL: columns descending
                         constexpr int i = decltype(ic)::value;
-                        line(h, qb, std::integral_constant<int, 2 * kColChunk - 1 - i>{}, i == 0,
+                        line(h, qb, std::integral_constant<int, PNCH * kColChunk - 1 - i>{}, i == 0,
                              std::integral_constant<int, 2>{});
                     });
                 }
@@ -542,7 +547,12 @@ hipError_t launch_slice(const ScanArgs& a, hipStream_t stream) {
     p.y = static_cast<uint16_t*>(a.y);
     p.B = a.B; p.C = a.C; p.H = a.H; p.W = a.W; p.Cw = a.C / a.cpw; p.cpw = a.cpw; p.groups = a.groups;
     p.dirs = a.dirs;
-    hipLaunchKernelGGL(slice_scan_kernel, dim3((unsigned)(a.B * a.C)), dim3(kSliceThreads), 0, stream, p);
+    // the instantiation whose LR/RL pair matches the column groups (8 columns:
+    // one piece; otherwise two, which 16-column groups use)
+    if (!(a.dirs & 12u) || a.W != a.groups * kColChunk)
+        hipLaunchKernelGGL(slice_scan_kernel<2>, dim3((unsigned)(a.B * a.C)), dim3(kSliceThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(slice_scan_kernel<1>, dim3((unsigned)(a.B * a.C)), dim3(kSliceThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -209,6 +209,9 @@ EDGE_SLICE = [
     (1, 2, 64, 64, 12, 8, 1),       # LR first then RL over 8-column groups
     (1, 2, 32, 128, 8, 8, 1),       # RL alone
     (1, 2, 128, 128, 4, 16, 1),     # LR alone, 8-column groups
+    (1, 2, 128, 128, 15, 16, 1),    # 8-column groups: LR with RL writing the output
+    (2, 2, 64, 64, 13, 8, 2),       # TB, then LR with RL over 8-column groups
+    (1, 2, 96, 128, 12, 16, 1),     # LR first with RL over 8-column groups
 ]
 
 
