@@ -795,11 +795,12 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def time_other_workloads(skip, dev, warm=5, steps=20):
+def time_other_workloads(skip, dev, warm=20, steps=200):
     """Forward time of every other workload of the suite, for context: inputs
     drawn on the device with the workloads' distributions (x ~ N(0, 1),
-    lambda and u ~ U(0, 1), raw taps ~ N(0, 1)); 20 back-to-back calls on one
-    buffer set after 5 untimed ones, HIP events on the launch stream."""
+    lambda and u ~ U(0, 1), raw taps ~ N(0, 1)); 200 back-to-back calls on one
+    buffer set after 20 untimed ones (the GPU's clocks settle over the first
+    few dozen calls), HIP events on the launch stream."""
     import torch
     import linear_spatial_propagation_amd as gspn
     from linear_spatial_propagation_amd import _lib
@@ -836,9 +837,16 @@ def time_other_workloads(skip, dev, warm=5, steps=20):
         torch.cuda.synchronize(dev)
         us = e0.elapsed_time(e1) * 1e3 / steps
         nbytes = algorithmic_bytes(B, C, H, W, 15, c["groups"], c["cpw"], c["dtype"])
-        res[name] = {"path": {1: "fused", 2: "general", 3: "slice"}[
-                         gspn.select_path(B, C, H, W, groups=c["groups"], ch_per_weight=c["cpw"],
-                                          dtype=_lib.GSPN_BF16 if c["dtype"] == "bf16" else _lib.GSPN_F32)],
+        path = {1: "fused", 2: "general", 3: "slice"}[
+            gspn.select_path(B, C, H, W, groups=c["groups"], ch_per_weight=c["cpw"],
+                             dtype=_lib.GSPN_BF16 if c["dtype"] == "bf16" else _lib.GSPN_F32)]
+        # the general path runs the line kernels where they hold the shape (the
+        # backward's condition), else one scan per line
+        if path == "general":
+            path += " (line kernels)" if _lib.bwd_supported(B, C, H, W, groups=c["groups"], ch_per_weight=c["cpw"],
+                                                             dtype=_lib.GSPN_BF16 if c["dtype"] == "bf16"
+                                                             else _lib.GSPN_F32) == 0 else " (per line)"
+        res[name] = {"path": path,
                      "us_per_step": round(us, 2), "gbps": round(nbytes / us / 1e3, 1),
                      "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
         del x, w, lam, u, y
