@@ -195,7 +195,7 @@ EDGE_SLICE = [
     # (B, C, H, W, dirs, groups, cpw)
     (1, 4, 128, 128, 15, 8, 1),     # the 2K local workload's slices
     (2, 3, 96, 64, 15, 8, 3),       # 12-line row groups, shared weights
-    (1, 2, 128, 128, 15, 16, 1),    # two groups per wave
+    (1, 2, 128, 128, 15, 16, 1),    # two groups per wave; 8-column groups: LR with RL writing the output
     (1, 2, 128, 128, 3, 32, 2),     # row directions only, 4-line groups
     (1, 2, 72, 128, 12, 8, 1),      # column directions only, idle lanes
     (1, 2, 48, 64, 15, 8, 1),       # 6-line row groups, 8-line column groups
@@ -209,7 +209,7 @@ EDGE_SLICE = [
     (1, 2, 64, 64, 12, 8, 1),       # LR first then RL over 8-column groups
     (1, 2, 32, 128, 8, 8, 1),       # RL alone
     (1, 2, 128, 128, 4, 16, 1),     # LR alone, 8-column groups
-    (1, 2, 128, 128, 15, 16, 1),    # 8-column groups: LR with RL writing the output
+    (1, 2, 64, 128, 9, 16, 1),      # TB, then RL alone over 8-column groups
     (2, 2, 64, 64, 13, 8, 2),       # TB, then LR with RL over 8-column groups
     (1, 2, 96, 128, 12, 16, 1),     # LR first with RL over 8-column groups
 ]
