@@ -610,6 +610,17 @@ __device__ __forceinline__ void fused_scan_body(const FusedParams& prm, const in
             constexpr int kBlocks = kColRegionBytes / 1024;   // 1 KB per wave-wide copy
             static_assert(kColRegionBytes % 1024 == 0, "whole 1 KB blocks");
             char* region = reinterpret_cast<char*>(lds) + kRowStageBytes + (d - 2) * kColRegionBytes;
+            // The first channel's x / lambda / u rows are requested before the
+            // copies, so that they travel with them.  Requested after the
+            // copies, they started only once a wait for the copies (which the
+            // compiler places before it reuses the copies' address registers)
+            // had passed, and the wait below then took a second memory round
+            // trip: per-wave timestamps showed the column waves ending the
+            // prologue last in every workgroup.  cls56 166-168 -> 161-165 us
+            // on one GPU, same bits; cgspn1k unchanged.
+            load_rows(gx, c_begin, x1);
+            load_rows(glam, c_begin, l1);
+            load_rows(gu, c_begin, u0);
             if (on) {
                 const T* src = wsrc.dir(d);
                 const int vpr = W / N;   // 16-byte pieces per row
@@ -627,9 +638,6 @@ __device__ __forceinline__ void fused_scan_body(const FusedParams& prm, const in
 #endif
                 }
             }
-            load_rows(gx, c_begin, x1);
-            load_rows(glam, c_begin, l1);
-            load_rows(gu, c_begin, u0);
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies have landed in LDS
             const bool has1 = p < m;
             static_for<0, kS / 8>([&](auto gc) {
