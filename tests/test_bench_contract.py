@@ -1,4 +1,5 @@
-"""bench.py's contract, checked without a GPU: one GPU only, and the
+"""bench.py's contract, checked without a GPU: one GPU only, the committed
+profiles recorded from the current kernel sources, and the
 algorithmic byte count of the default workload worked out by hand.
 
 cgspn1k: B = 32, C = 128, 64 x 64, cpw = 8, bf16, four directions, one group.
@@ -37,3 +38,25 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_committed_profiles_match_the_kernel_sources():
+    # every summary under profiles/ that carries a kernel source hash was
+    # recorded from the sources as they stand (bench.py reports no counter
+    # traffic for a kernel that changed since its counters were taken)
+    import glob
+    checked = 0
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.txt"))):
+        recorded = None
+        with open(path) as f:
+            for line in f:
+                if line.startswith("kernel_source_hash:"):
+                    recorded = line.split(":", 1)[1].strip()
+        if recorded is None:
+            continue
+        kernel = next(k for k in ("fused_scan_kernel", "fused_bwd_kernel", "slice_scan_kernel")
+                      if os.path.basename(path).startswith(k))
+        pass_ = "bwd" if kernel == "fused_bwd_kernel" else "fwd"
+        assert recorded == bench.kernel_source_hash(pass_, kernel), f"{path} was recorded from other sources"
+        checked += 1
+    assert checked >= 6
