@@ -27,6 +27,12 @@ directly with argument tuples built once.
 device_copy_gbps: a plain 512 MiB device-to-device copy on the same GPU
 (read + write bytes per second), the practical streaming ceiling, for context.
 
+other_workloads: the forward of every other workload (fused, slice or line
+kernels, as the library picks), each with its backward (`bwd`); backward: the
+default workload's backward.  Device-drawn inputs of the workloads'
+distributions, back-to-back calls on one buffer set; reported beside the
+headline, not part of it.
+
 value = algorithmic bytes x K / elapsed time (GB/s, 1e9 B/s).  Algorithmic
 bytes count each input once, y once, and only the taps the method consumes:
     s * (|x| + |lam| + |u| + |y|) + s * B * Cw * sum_d (n_d - g) * (3 m_d - 2)
@@ -790,6 +796,7 @@ def main():
     if (not bwd and args.variant == "none" and batched == 1 and not args.profile_run and not args.copy_calibration
             and args.others):
         out["other_workloads"] = time_other_workloads(args.config, dev)
+        out["backward"] = time_backward(cfgd, *bwd_inputs(cfgd, dev), dev)
     if not args.no_cpu and not args.profile_run and args.variant == "none" and batched == 1:
         out["cpu_baseline"] = cpu_baseline(args.config, backward=bwd)
     print(json.dumps(out), flush=True)
@@ -800,7 +807,10 @@ def time_other_workloads(skip, dev, warm=20, steps=200):
     drawn on the device with the workloads' distributions (x ~ N(0, 1),
     lambda and u ~ U(0, 1), raw taps ~ N(0, 1)); 200 back-to-back calls on one
     buffer set after 20 untimed ones (the GPU's clocks settle over the first
-    few dozen calls), HIP events on the launch stream."""
+    few dozen calls), HIP events on the launch stream.  Each entry also
+    carries the workload's backward (`bwd`: one gspn_scan_bwd call per step,
+    gy ~ N(0, 1), 50 calls after 10, outputs preallocated), whose algorithmic
+    bytes are algorithmic_bytes_bwd's."""
     import torch
     import linear_spatial_propagation_amd as gspn
     from linear_spatial_propagation_amd import _lib
@@ -849,9 +859,54 @@ def time_other_workloads(skip, dev, warm=20, steps=200):
         res[name] = {"path": path,
                      "us_per_step": round(us, 2), "gbps": round(nbytes / us / 1e3, 1),
                      "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
-        del x, w, lam, u, y
+        del y
+        res[name]["bwd"] = time_backward(c, x, w, lam, u, g, dev)
+        del x, w, lam, u
         torch.cuda.empty_cache()
     return res
+
+
+def bwd_inputs(c, dev):
+    """Device-drawn inputs of one workload for time_backward."""
+    import torch
+    B, C, H, W = c["B"], c["C"], c["H"], c["W"]
+    dt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
+    g = torch.Generator(device=dev)
+    g.manual_seed(c["seed"])
+    x = torch.randn((B, C, H, W), generator=g, device=dev, dtype=torch.float32).to(dt)
+    w = torch.randn((4, B, C // c["cpw"], 3, H, W), generator=g, device=dev, dtype=torch.float32).to(dt)
+    lam = torch.rand((B, C, H, W), generator=g, device=dev, dtype=torch.float32).to(dt)
+    u = (torch.ones((B, C, H, W), device=dev, dtype=dt) if c["u_ones"] else
+         torch.rand((B, C, H, W), generator=g, device=dev, dtype=torch.float32).to(dt))
+    return x, w, lam, u, g
+
+
+def time_backward(c, x, w, lam, u, g, dev, warm=10, steps=50):
+    """Backward time of one workload (see time_other_workloads)."""
+    import torch
+    import linear_spatial_propagation_amd as gspn
+    B, C, H, W = c["B"], c["C"], c["H"], c["W"]
+    gy = torch.randn(x.shape, generator=g, device=dev, dtype=torch.float32).to(x.dtype)
+    outs = (torch.empty_like(x), torch.empty_like(w), torch.empty_like(x), torch.empty_like(x))
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gspn.scan_bwd(x, w, lam, u, gy, dirs=15, groups=c["groups"], ch_per_weight=c["cpw"], out=outs)
+    for _ in range(warm):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = algorithmic_bytes_bwd(B, C, H, W, 15, c["groups"], c["cpw"], c["dtype"])
+    del gy, outs
+    return {"path": "fused" if max(H, W) <= 64 else "line kernels",
+            "us_per_step": round(us, 2), "gbps": round(nbytes / us / 1e3, 1),
+            "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
 
 
 if __name__ == "__main__":
