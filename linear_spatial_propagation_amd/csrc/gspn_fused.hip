@@ -589,7 +589,13 @@ __device__ __forceinline__ void fused_scan_body(const FusedParams& prm, const in
 #ifndef GSPN_SLOTS
 #define GSPN_SLOTS 8
 #endif
-        constexpr int kAhead = GSPN_TAP_AHEAD;               // chunks loaded up front
+        // Chunks loaded up front: three, or two when a weight set has one
+        // channel (the instantiation without non-temporal rows, NTR false):
+        // there the taps are three quarters of the bytes and the first chunk
+        // arrives sooner when fewer compete with it (cls56 155.5-156.0 ->
+        // 153.4-153.9 us in steady state on one GPU, same bits; cgspn1k is
+        // best with three).
+        constexpr int kAhead = NTR ? GSPN_TAP_AHEAD : 2;
         constexpr int kTapItems = (kNCh - kAhead) * kLd;     // items [0, kTapItems): tap loads of chunks kAhead..
         constexpr int kItems = kTapItems + 3 * kMaxIt;       // then x, lambda, u rows
         constexpr int kSlots = (kItems + kNCh - 1) / kNCh > GSPN_SLOTS ? (kItems + kNCh - 1) / kNCh : GSPN_SLOTS;
