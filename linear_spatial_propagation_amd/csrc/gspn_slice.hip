@@ -129,6 +129,13 @@ void slice_scan_kernel(SliceParams prm) {
     __shared__ float xlp[kSliceMax * kAccPitch];   // lambda * x, written by the first direction
     const int tid = threadIdx.x;
     const int wave = uniform(tid >> 6), lane = tid & 63;
+    // Waves w and w + 4 share a SIMD and get the same work; at equal priority
+    // the SIMD favours the older wave, and per-wave timestamps showed waves
+    // 4-7 finishing the column pair about 6 us after waves 0-3.  Raising the
+    // younger waves' issue priority evens that out: local2k 265.6-266.6 ->
+    // 262.4-263.0 us on one GPU (waves 0-3 raised instead: 264.3-265.0),
+    // same bits.
+    if (wave >= 4) __builtin_amdgcn_s_setprio(1);
     const int H = prm.H, W = prm.W, C = prm.C, B = prm.B;
     const size_t HW = (size_t)H * W;
     const int slice = blockIdx.x;
