@@ -169,10 +169,13 @@ struct LineData {
 
 // D: lines loaded ahead (deeper for long lines: fewer waves share the GPU
 // then, so each must keep more bytes in flight).
-// SPLIT = 2: a line is held by the two waves of a 128-thread workgroup, each
-// owning 64 K consecutive positions; after every line they swap the state at
-// their common edge through LDS (one barrier per line).  Halving the unit of
-// work balances launches whose scans barely exceed one wave per SIMD.
+// SPLIT > 1: a line is held by the SPLIT waves of a workgroup, each owning
+// 64 K consecutive positions; after every line each wave publishes the
+// states at both of its ends through LDS and takes its neighbours' (one
+// barrier per line).  Splitting the unit of work balances launches whose
+// scans barely exceed one wave per SIMD: hires512's 1280 scans as 2560 waves
+// of 4 positions per lane left half the SIMDs with a third wave; as 5120
+// waves of 2 positions (5 per SIMD) its scan is about 1% faster (same bits).
 // G: channels per wave, G consecutive channels of one weight set (cpw a
 // multiple of G): the taps are loaded and normalised once per pixel and
 // drive the G channels' scans (the channel-shared weights of the GSPN-2
@@ -182,8 +185,8 @@ template <typename T, int K, int D, int SPLIT, int G>
 __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
     static_assert(SPLIT == 1 || G == 1, "split lines scan one channel per wave");
     const int lane = threadIdx.x & 63;
-    const int half = SPLIT == 2 ? uniform(threadIdx.x >> 6) : 0;   // which part of the line
-    const int unit = SPLIT == 2 ? (int)blockIdx.x : (int)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+    const int half = SPLIT >= 2 ? uniform(threadIdx.x >> 6) : 0;   // which part of the line
+    const int unit = SPLIT >= 2 ? (int)blockIdx.x : (int)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
     const int C = prm.C, B = prm.B;
     const int CG = C / G;   // channel groups
     if (unit >= prm.nd * B * CG) return;   // whole wave
@@ -259,10 +262,10 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
         for (int e = 0; e < K; ++e) h[g][e] = 0.0f;
     // SPLIT: the neighbour part's state at the common edge (position
     // 64K - 1 or 64K of the line), from the previous line
-    __shared__ float edge[2][2];   // [line parity][part]
-    float bnd = 0.0f;
-    const bool takes_left = SPLIT == 2 && half == 1 && lane == 0;
-    const bool takes_right = SPLIT == 2 && half == 0 && lane == 63;
+    __shared__ float edge[2][SPLIT > 1 ? SPLIT : 1][2];   // [line parity][part][first, last position]
+    float bndl = 0.0f, bndr = 0.0f;
+    const bool takes_left = SPLIT >= 2 && half > 0 && lane == 0;
+    const bool takes_right = SPLIT >= 2 && half < SPLIT - 1 && lane == 63;
 
     // D lines per iteration; steps past the last line (when D does not
     // divide n) compute on clamped data and store nothing
@@ -319,13 +322,13 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
                 for (int g = 0; g < G; ++g) {
                     float left = from_left(h[g][K - 1]);
                     float right = from_right(h[g][0]);
-                    if constexpr (SPLIT == 2) {
+                    if constexpr (SPLIT >= 2) {
                         // the lane exchange runs in every lane before the edge
                         // lanes take the other part's value: sunk into a branch
                         // it would read the masked-off edge lanes as 0
                         asm volatile("" : "+v"(left), "+v"(right));
-                        left = takes_left ? bnd : left;
-                        right = takes_right ? bnd : right;
+                        left = takes_left ? bndl : left;
+                        right = takes_right ? bndr : right;
                     }
 #pragma unroll
                     for (int e = 0; e < K; ++e) {
@@ -341,15 +344,17 @@ __global__ __launch_bounds__(256) void line_scan_kernel(LineParams prm) {
             for (int g = 0; g < G; ++g)
 #pragma unroll
                 for (int e = 0; e < K; ++e) h[g][e] = hn[g][e];
-            if constexpr (SPLIT == 2) {
+            if constexpr (SPLIT >= 2) {
                 // swap the edge states; the parity double-buffers the slots so
                 // that one barrier per line suffices
                 const int par = i & 1;
-                if (lane == (half == 0 ? 63 : 0)) edge[par][half] = half == 0 ? h[0][K - 1] : h[0][0];
+                if (lane == 0) edge[par][half][0] = h[0][0];
+                if (lane == 63) edge[par][half][1] = h[0][K - 1];
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
                 __builtin_amdgcn_s_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-                bnd = edge[par][half ^ 1];
+                bndl = half > 0 ? edge[par][half > 0 ? half - 1 : 0][1] : 0.0f;
+                bndr = half < SPLIT - 1 ? edge[par][half < SPLIT - 1 ? half + 1 : 0][0] : 0.0f;
             }
             {
                 // unconditional store (a store under a divergent branch also
@@ -667,8 +672,8 @@ template <typename T>
 void launch_line_scan(const LineParams& p, hipStream_t stream) {
     const long units = (long)p.nd * p.B * p.C;
     const int m = p.H > p.W ? p.H : p.W;
-    if (m > 256) {   // sides above 256: two waves of 4 positions per lane hold a line
-        hipLaunchKernelGGL((line_scan_kernel<T, 4, kDepthK4, 2, 1>), dim3((unsigned)units), dim3(128), 0, stream, p);
+    if (m > 256) {   // sides above 256: four waves of 2 positions per lane hold a line
+        hipLaunchKernelGGL((line_scan_kernel<T, 2, kDepthK4, 4, 1>), dim3((unsigned)units), dim3(256), 0, stream, p);
         return;
     }
     const int G = line_scan_channels(p);
