@@ -8,8 +8,10 @@
 //     as contiguous rows.  64 x 64 tiles through LDS, 16-byte accesses.
 //  2. line_scan_kernel<K>: one wave per (direction, b, c) scan; lane l owns
 //     K consecutive positions of the line (K * 64 >= line length), so a line
-//     is one wave, the state lives in K VGPRs per lane, and the neighbours
-//     across lanes come from DPP wave shifts.  The inputs of the next kDepth
+//     is one wave (lines longer than 256: four waves of 2 positions per lane
+//     that exchange their end states once per line), the state lives in K
+//     VGPRs per lane, and the neighbours across lanes come from DPP wave
+//     shifts.  The inputs of the next kDepth
 //     lines are prefetched into registers with 16-byte (or K-element) loads;
 //     taps are normalised as they are consumed (3 exp + 1 rcp per pixel).
 //     Each direction writes h, line-major, to its own fp32 plane.
